@@ -1,0 +1,122 @@
+"""Seeded synthetic workloads: shapes and random draws only.
+
+This module holds none of the NF4 arithmetic.  It is the one place both the
+oracle-side tests and the GPU-side tests/benchmark take their inputs from, so
+the two sides see identical bytes.  Every draw comes from
+numpy.random.default_rng(SeedSequence([base, workload, layer, proj, kind])).
+
+Shapes are those of the models the pages measure on (Llama-3.1-8B streaming in
+Soup issue #842 "Why"; Qwen2.5-32B in bitsandbytes #2034 "The evidence,
+briefly"; OLMoE-1B-7B experts in the Experts PR "Measurements").  No
+checkpoint or dataset is used: weights are 0.02 * N(0, 1) fp32, activations
+and output gradients are N(0, 1) rounded to bf16 by torch.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+BASE_SEED = 20251202
+
+# workload ids inside the seed sequence
+W_TINY, W_LLAMA, W_DECODE, W_QWEN, W_OLMOE = 0, 1, 2, 3, 4
+# tensor kinds inside the seed sequence
+K_WEIGHT, K_X, K_GY, K_ROUTE = 0, 1, 2, 3
+
+
+@dataclass(frozen=True)
+class Proj:
+    name: str
+    N: int   # out features (rows of W)
+    K: int   # in features
+
+
+# Llama-3.1-8B projections, W in the F.linear [out, in] layout.
+LLAMA_8B = (
+    Proj("q", 4096, 4096), Proj("k", 1024, 4096), Proj("v", 1024, 4096),
+    Proj("o", 4096, 4096), Proj("gate", 14336, 4096), Proj("up", 14336, 4096),
+    Proj("down", 4096, 14336),
+)
+LLAMA_LAYERS = 32
+LLAMA_M = 512            # batch 1, S = 512
+DECODE_MS = (1, 8, 32)
+
+# Qwen-32B-shaped projections at M = 2048.
+QWEN_32B = (
+    Proj("q", 5120, 5120), Proj("k", 1024, 5120), Proj("v", 1024, 5120),
+    Proj("o", 5120, 5120), Proj("gate", 27648, 5120), Proj("up", 27648, 5120),
+    Proj("down", 5120, 27648),
+)
+QWEN_M = 2048
+
+# OLMoE-1B-7B experts: 64 experts, hidden 2048, intermediate 1024, top-8, 512 tokens.
+OLMOE_E, OLMOE_HIDDEN, OLMOE_INTER, OLMOE_TOPK, OLMOE_TOKENS = 64, 2048, 1024, 8, 512
+
+# Tiny NF4 linear (non-nested): M = 64, N = 128, K = 256.
+TINY_M, TINY_N, TINY_K = 64, 128, 256
+
+
+def rng(*key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([BASE_SEED, *key]))
+
+
+def weight_f32(N: int, K: int, *key: int, std: float = 0.02) -> np.ndarray:
+    """W [N, K] fp32 ~ std * N(0, 1)."""
+    g = rng(*key, K_WEIGHT)
+    return (g.standard_normal((N, K), dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def normal_bf16(M: int, C: int, *key: int) -> torch.Tensor:
+    """[M, C] bf16 CPU tensor of N(0, 1) draws (torch rounds to bf16)."""
+    g = rng(*key)
+    a = g.standard_normal((M, C), dtype=np.float32)
+    return torch.from_numpy(a).to(torch.bfloat16)
+
+
+def x_bf16(M: int, K: int, *key: int) -> torch.Tensor:
+    return normal_bf16(M, K, *key, K_X)
+
+
+def grad_y_bf16(M: int, N: int, *key: int) -> torch.Tensor:
+    return normal_bf16(M, N, *key, K_GY)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bf16 bit patterns of a CPU bf16 tensor, as uint16 (no arithmetic)."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def olmoe_routing(tokens: int = OLMOE_TOKENS, experts: int = OLMOE_E, topk: int = OLMOE_TOPK,
+                  *key: int):
+    """Top-k distinct experts per token, uniform without replacement.
+
+    Returns (order, expert_of_row, offsets): `order` maps each sorted row to
+    its token, rows are stably sorted by expert, offsets[e] is the first row
+    of expert e (length experts + 1).
+    """
+    g = rng(W_OLMOE, *key, K_ROUTE)
+    choice = np.argsort(g.random((tokens, experts)), axis=1)[:, :topk]   # distinct per token
+    tok = np.repeat(np.arange(tokens), topk)
+    exp = choice.reshape(-1)
+    perm = np.argsort(exp, kind="stable")
+    counts = np.bincount(exp, minlength=experts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return tok[perm], exp[perm], offsets
+
+
+def gpu_weight_f32(N: int, K: int, seed: int, device="cuda", std: float = 0.02) -> torch.Tensor:
+    """W [N, K] fp32 ~ std * N(0, 1) drawn on the device by torch's seeded
+    Philox generator (used where host draws would be too slow: the 32-layer
+    benchmark stack)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(BASE_SEED * 1000 + seed)
+    return torch.randn((N, K), generator=g, device=device, dtype=torch.float32).mul_(std)
+
+
+def gpu_normal_bf16(M: int, C: int, seed: int, device="cuda") -> torch.Tensor:
+    g = torch.Generator(device=device)
+    g.manual_seed(BASE_SEED * 1000 + seed)
+    return torch.randn((M, C), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
