@@ -229,6 +229,22 @@ def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def bf16_rne_bits_from_f64(x: np.ndarray) -> np.ndarray:
+    """bf16 bits of fp64 values by ONE round-to-nearest-even (normal range).
+
+    The matmul output is returned in bf16, the dtype of the inputs (the
+    F.linear convention kept by Soup #842, "Design sketch"), so the reference
+    output is the exact product rounded once.  Rounding through fp32 first
+    would round twice; here the fp64 significand is cut to bf16's 8 bits
+    directly (bit 45 is the last kept bit), then the exact value is narrowed.
+    """
+    u = np.ascontiguousarray(x, dtype=F64).view(np.uint64)
+    r = ((u + np.uint64(0x0FFFFFFFFFFF) + ((u >> np.uint64(45)) & np.uint64(1)))
+         >> np.uint64(45)) << np.uint64(45)
+    v = r.view(F64).astype(F32)                 # exact: at most 8 significant bits
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Exact widening of bf16 bit patterns to fp32."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(F32)

@@ -149,6 +149,25 @@ def test_bf16_rne_special_cases():
     assert np.array_equal(O.bf16_bits_to_f32(b)[:2], np.array([1.0, 1.0], F32))
 
 
+def test_bf16_single_rounding_from_f64():
+    # 1 + 2^-8 + 2^-30 lies just above a bf16 tie: one rounding goes up, while
+    # rounding through fp32 first lands exactly on the tie and goes to even.
+    v = np.array([1.0 + 2 ** -8 + 2 ** -30, -(1.0 + 2 ** -8 + 2 ** -30)])
+    assert list(O.bf16_rne_bits_from_f64(v)) == [0x3F81, 0xBF81]
+    assert list(O.bf16_rne_bits(v.astype(F32))) == [0x3F80, 0xBF80]
+    # on values exactly representable in fp32 both routes agree
+    g = np.random.default_rng(12)
+    x = (g.standard_normal(20000) * 10.0 ** g.integers(-3, 3, 20000)).astype(F32)
+    assert np.array_equal(O.bf16_rne_bits_from_f64(x.astype(np.float64)), O.bf16_rne_bits(x))
+    # and the result is the nearest bf16 value (brute force over neighbours)
+    y = g.standard_normal(5000)
+    b = O.bf16_rne_bits_from_f64(y)
+    val = O.bf16_bits_to_f32(b).astype(np.float64)
+    for d in (-1, 1):
+        nb = O.bf16_bits_to_f32((b.astype(np.int32) + d).astype(np.uint16)).astype(np.float64)
+        assert np.all(np.abs(y - val) <= np.abs(y - nb))
+
+
 # --- nested statistics ---------------------------------------------------------
 
 def test_offset_is_the_mean_in_fixed_order():
