@@ -1,0 +1,249 @@
+// extern "C" entry points of libnf4.so (declared and documented in nf4.h):
+// argument validation, launch planning and path counters.  No entry point
+// allocates, frees or synchronises.
+#include <atomic>
+#include <climits>
+
+#include "../../include/nf4.h"
+#include "nf4_internal.hpp"
+
+namespace nf4 {
+
+static std::atomic<int64_t> g_path_counts[NF4_PATH_COUNT];
+
+void count_path(int path) {
+  if (path >= 0 && path < NF4_PATH_COUNT) g_path_counts[path].fetch_add(1, std::memory_order_relaxed);
+}
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks shared by every call that takes the W-args.
+int check_w(const uint8_t* packed, const void* absmax, const float* nested_absmax,
+            const float* nested_offset, const float* code16, const float* ncode, int64_t N,
+            int64_t K) {
+  if (!packed || !absmax || !code16) return NF4_ERR_NULL;
+  if (nested_absmax && (!nested_offset || !ncode)) return NF4_ERR_NULL;
+  if (N < 0 || K < 0) return NF4_ERR_SHAPE;
+  if (N > 0 && K > INT64_MAX / N) return NF4_ERR_SHAPE;
+  if ((N * K) % 2) return NF4_ERR_SHAPE;
+  if (!aligned16(packed)) return NF4_ERR_ALIGN;
+  return NF4_OK;
+}
+
+int check_gemm_shape(int64_t M, int64_t N, int64_t K, bool bwd) {
+  if (M < 0) return NF4_ERR_SHAPE;
+  if (K % 64) return NF4_ERR_UNSUPPORTED;   // every 64-block must lie in one row of W
+  if (bwd && (N % 8)) return NF4_ERR_UNSUPPORTED;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return NF4_ERR_UNSUPPORTED;
+  return NF4_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+
+int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed,
+                  const void* absmax, const float* nested_absmax, const float* nested_offset,
+                  const float* code16, const float* ncode, int64_t N, int64_t K, void* C,
+                  void* ws, size_t ws_bytes, void* stream) {
+  const bool bwd = kind == GemmKind::kBwdInput;
+  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K);
+  if (st) return st;
+  if (!A || !C) return NF4_ERR_NULL;
+  st = check_gemm_shape(M, N, K, bwd);
+  if (st) return st;
+  if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
+  if (M == 0 || N == 0 || K == 0) {
+    if (M > 0 && (bwd ? K : N) > 0) {
+      // an empty contraction: the product is all zeros
+      const size_t bytes = static_cast<size_t>(M) * static_cast<size_t>(bwd ? K : N) * 2;
+      return to_status(hipMemsetAsync(C, 0, bytes, static_cast<hipStream_t>(stream)));
+    }
+    return NF4_OK;
+  }
+  const GemmPlan plan = plan_gemm(kind, M, N, K, device_cu_count());
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return NF4_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && !aligned16(ws)) return NF4_ERR_ALIGN;
+  const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
+  return to_status(launch_gemm(kind, plan, A, M, w, C, ws, static_cast<hipStream_t>(stream)));
+}
+
+int grouped_common(GemmKind kind, const void* A, const int32_t* offsets, int32_t E,
+                   int64_t total_M, const uint8_t* packed, const void* absmax,
+                   const float* nested_absmax, const float* nested_offset, const float* code16,
+                   const float* ncode, int64_t N, int64_t K, void* C, void* ws, size_t ws_bytes,
+                   void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const bool bwd = kind == GemmKind::kBwdInput;
+  if (E < 1) return NF4_ERR_SHAPE;
+  if (N < 0 || K < 0 || (N > 0 && E > INT64_MAX / N)) return NF4_ERR_SHAPE;
+  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode,
+                   static_cast<int64_t>(E) * N, K);
+  if (st) return st;
+  if (!A || !C || !offsets) return NF4_ERR_NULL;
+  st = check_gemm_shape(total_M, N, K, bwd);
+  if (st) return st;
+  if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
+  if (total_M == 0 || N == 0 || K == 0) {
+    if (total_M > 0 && (bwd ? K : N) > 0) {
+      const size_t bytes = static_cast<size_t>(total_M) * static_cast<size_t>(bwd ? K : N) * 2;
+      return to_status(hipMemsetAsync(C, 0, bytes, static_cast<hipStream_t>(stream)));
+    }
+    return NF4_OK;
+  }
+  const GemmPlan plan = plan_grouped(kind, total_M, N, K, E);
+  const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
+  return to_status(launch_grouped(kind, plan, A, offsets, E, total_M, w, C,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+}  // namespace nf4
+
+using namespace nf4;
+
+extern "C" {
+
+int nf4_quantize(const void* w, int w_dtype, int64_t N, int64_t K, const float* code16,
+                 const float* nested_code256, uint8_t* packed, void* absmax, float* nested_absmax,
+                 float* nested_offset, void* ws, size_t ws_bytes, void* stream) {
+  if (w_dtype != NF4_DTYPE_F32 && w_dtype != NF4_DTYPE_BF16) return NF4_ERR_DTYPE;
+  if (!w || !code16 || !packed || !absmax) return NF4_ERR_NULL;
+  const bool nested = nested_code256 != nullptr;
+  if (nested && (!nested_absmax || !nested_offset)) return NF4_ERR_NULL;
+  if (N < 0 || K < 0) return NF4_ERR_SHAPE;
+  if (N > 0 && K > INT64_MAX / N) return NF4_ERR_SHAPE;
+  const int64_t n = N * K;
+  if (n % 2) return NF4_ERR_SHAPE;
+  if (n == 0) return NF4_OK;
+  if (!aligned16(packed) || !aligned16(w)) return NF4_ERR_ALIGN;
+  const size_t need = quantize_ws_bytes(n, nested);
+  if (need > 0 && (!ws || ws_bytes < need)) return NF4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return NF4_ERR_ALIGN;
+  const hipError_t e = launch_quantize(w, w_dtype == NF4_DTYPE_BF16, n, code16, nested_code256,
+                                       packed, absmax, nested_absmax, nested_offset, ws,
+                                       static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) count_path(NF4_PATH_QUANTIZE);
+  return e == hipSuccess ? NF4_OK : NF4_ERR_HIP;
+}
+
+int nf4_dequantize(const uint8_t* packed, const void* absmax, const float* nested_absmax,
+                   const float* nested_offset, const float* code16, const float* nested_code256,
+                   int64_t N, int64_t K, int out_dtype, void* out, void* stream) {
+  if (out_dtype != NF4_DTYPE_F32 && out_dtype != NF4_DTYPE_BF16) return NF4_ERR_DTYPE;
+  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N, K);
+  if (st) return st;
+  if (!out) return NF4_ERR_NULL;
+  if (!aligned16(out)) return NF4_ERR_ALIGN;
+  const int64_t n = N * K;
+  if (n == 0) return NF4_OK;
+  const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N, K};
+  const hipError_t e = launch_dequantize(w, n, out_dtype == NF4_DTYPE_BF16, out,
+                                         static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) count_path(NF4_PATH_DEQUANTIZE);
+  return e == hipSuccess ? NF4_OK : NF4_ERR_HIP;
+}
+
+int nf4_matmul_fwd(const void* x, int64_t M, const uint8_t* packed, const void* absmax,
+                   const float* nested_absmax, const float* nested_offset, const float* code16,
+                   const float* nested_code256, int64_t N, int64_t K, void* y, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return matmul_common(GemmKind::kFwd, x, M, packed, absmax, nested_absmax, nested_offset,
+                       code16, nested_code256, N, K, y, ws, ws_bytes, stream);
+}
+
+int nf4_matmul_bwd_input(const void* grad_y, int64_t M, const uint8_t* packed,
+                         const void* absmax, const float* nested_absmax,
+                         const float* nested_offset, const float* code16,
+                         const float* nested_code256, int64_t N, int64_t K, void* grad_x,
+                         void* ws, size_t ws_bytes, void* stream) {
+  return matmul_common(GemmKind::kBwdInput, grad_y, M, packed, absmax, nested_absmax,
+                       nested_offset, code16, nested_code256, N, K, grad_x, ws, ws_bytes,
+                       stream);
+}
+
+int nf4_grouped_matmul_fwd(const void* x, const int32_t* offsets, int32_t E, int64_t total_M,
+                           const uint8_t* packed, const void* absmax, const float* nested_absmax,
+                           const float* nested_offset, const float* code16,
+                           const float* nested_code256, int64_t N, int64_t K, void* y, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return grouped_common(GemmKind::kFwd, x, offsets, E, total_M, packed, absmax, nested_absmax,
+                        nested_offset, code16, nested_code256, N, K, y, ws, ws_bytes, stream);
+}
+
+int nf4_grouped_matmul_bwd_input(const void* grad_y, const int32_t* offsets, int32_t E,
+                                 int64_t total_M, const uint8_t* packed, const void* absmax,
+                                 const float* nested_absmax, const float* nested_offset,
+                                 const float* code16, const float* nested_code256, int64_t N,
+                                 int64_t K, void* grad_x, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return grouped_common(GemmKind::kBwdInput, grad_y, offsets, E, total_M, packed, absmax,
+                        nested_absmax, nested_offset, code16, nested_code256, N, K, grad_x, ws,
+                        ws_bytes, stream);
+}
+
+size_t nf4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E) {
+  if (M < 0 || N < 0 || K < 0) return SIZE_MAX;
+  if (N > 0 && K > INT64_MAX / N) return SIZE_MAX;
+  switch (op) {
+    case NF4_OP_QUANTIZE:
+      return quantize_ws_bytes(N * K, true);
+    case NF4_OP_MATMUL_FWD:
+    case NF4_OP_MATMUL_BWD_INPUT: {
+      if (M == 0 || N == 0 || K == 0) return 0;
+      const GemmKind kind = op == NF4_OP_MATMUL_FWD ? GemmKind::kFwd : GemmKind::kBwdInput;
+      return plan_gemm(kind, M, N, K, device_cu_count()).ws_bytes;
+    }
+    case NF4_OP_GROUPED_FWD:
+    case NF4_OP_GROUPED_BWD_INPUT:
+      if (E < 1) return SIZE_MAX;
+      return 0;
+    default:
+      return SIZE_MAX;
+  }
+}
+
+int64_t nf4_packed_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || (N > 0 && K > INT64_MAX / N)) return -1;
+  return N * K / 2;
+}
+
+int64_t nf4_absmax_count(int64_t N, int64_t K) {
+  if (N < 0 || K < 0 || (N > 0 && K > INT64_MAX / N)) return -1;
+  return ceil_div(N * K, 64);
+}
+
+int64_t nf4_nested_count(int64_t N, int64_t K) {
+  const int64_t nb = nf4_absmax_count(N, K);
+  return nb < 0 ? -1 : ceil_div(nb, 256);
+}
+
+int64_t nf4_path_count(int path) {
+  if (path < 0 || path >= NF4_PATH_COUNT) return -1;
+  return g_path_counts[path].load(std::memory_order_relaxed);
+}
+
+void nf4_reset_path_counts(void) {
+  for (auto& c : g_path_counts) c.store(0, std::memory_order_relaxed);
+}
+
+const char* nf4_status_str(int status) {
+  switch (status) {
+    case NF4_OK: return "NF4_OK: success";
+    case NF4_ERR_NULL: return "NF4_ERR_NULL: a required pointer is NULL";
+    case NF4_ERR_SHAPE: return "NF4_ERR_SHAPE: invalid sizes";
+    case NF4_ERR_UNSUPPORTED: return "NF4_ERR_UNSUPPORTED: unsupported shape (K % 64, N % 8 or size limit)";
+    case NF4_ERR_ALIGN: return "NF4_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case NF4_ERR_WORKSPACE: return "NF4_ERR_WORKSPACE: workspace missing or too small";
+    case NF4_ERR_HIP: return "NF4_ERR_HIP: the HIP runtime reported an error";
+    case NF4_ERR_DTYPE: return "NF4_ERR_DTYPE: unknown dtype selector";
+    default: return "unknown NF4 status";
+  }
+}
+
+const char* nf4_version(void) { return "nf4-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (nf4_abi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nf4 {
+
+// The W-args of the ABI: one quantised tensor of N rows x K columns (for the
+// grouped calls, E*N rows; N and K are per expert).
+struct WArgs {
+  const uint8_t* packed;
+  const void* absmax;
+  const float* nested_absmax;  // NULL -> plain fp32 absmax
+  const float* nested_offset;
+  const float* code;           // 16 fp32
+  const float* ncode;          // 256 fp32 (nested only)
+  int64_t N, K;
+  bool nested() const { return nested_absmax != nullptr; }
+};
+
+// ---- codec -----------------------------------------------------------------
+size_t quantize_ws_bytes(int64_t n_elems, bool nested);
+hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n_elems, const float* code,
+                           const float* ncode, uint8_t* packed, void* absmax,
+                           float* nested_absmax, float* nested_offset, void* ws,
+                           hipStream_t stream);
+hipError_t launch_dequantize(const WArgs& w, int64_t n_elems, bool out_bf16, void* out,
+                             hipStream_t stream);
+
+// ---- fused matmuls ---------------------------------------------------------
+enum class GemmKind { kFwd, kBwdInput };
+
+// How one dense (non-grouped) call is split into launches.  A pure function
+// of (M, N, K, kind, compute units).
+struct GemmPlan {
+  int bm;          // rows of the activation tile
+  int splits;      // contraction split count (1 = none)
+  bool small_m;    // weight-streaming forward
+  size_t ws_bytes; // fp32 partials when splits > 1
+};
+int device_cu_count();
+GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus);
+GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int32_t E);
+
+hipError_t launch_gemm(GemmKind kind, const GemmPlan& plan, const void* A, int64_t M,
+                       const WArgs& w, void* C, void* ws, hipStream_t stream);
+hipError_t launch_grouped(GemmKind kind, const GemmPlan& plan, const void* A,
+                          const int32_t* offsets, int32_t E, int64_t total_M, const WArgs& w,
+                          void* C, hipStream_t stream);
+
+// path counters (defined in nf4_abi.hip)
+void count_path(int path);
+
+}  // namespace nf4

@@ -1,0 +1,78 @@
+"""GPU parity of the grouped (expert) forward and input gradient."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from nf4_bit_weight_amd import api
+from oracle import nf4_oracle as O
+
+from gpu_util import DEV, abs_bits, assert_close, ref_bits, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack(E, N, K, nested, seed):
+    w = WL.weight_f32(E * N, K, WL.W_OLMOE, seed)
+    ref = O.quantize_nf4(w, nested=nested)
+    return upload(ref, N, K, nested), ref_bits(ref, (E, N, K))
+
+
+@pytest.mark.parametrize("nested", [False, True])
+def test_grouped_ragged_and_empty_experts(nested):
+    E, N, K = 6, 136, 192
+    counts = np.array([3, 0, 70, 129, 0, 1])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(offsets[-1])
+    wq, wb = _stack(E, N, K, nested, 5)
+    x = WL.x_bf16(T, K, WL.W_OLMOE, 50)
+    gy = WL.grad_y_bf16(T, N, WL.W_OLMOE, 50)
+    off = torch.from_numpy(offsets).to(DEV)
+    y = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+    gx = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
+    xb, gyb, aw = WL.bf16_bits(x), WL.bf16_bits(gy), abs_bits(wb)
+    assert_close(y, O.grouped_matmul_fwd(xb, offsets, wb), "grouped y",
+                 O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
+    assert_close(gx, O.grouped_matmul_bwd_input(gyb, offsets, wb), "grouped grad_x",
+                 O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)
+
+
+def test_grouped_identity_rows():
+    """Each routed row is a unit vector: outputs are exact columns of W_hat_e."""
+    E, N, K = 4, 64, 128
+    wq, wb = _stack(E, N, K, True, 6)
+    counts = np.array([5, 9, 0, 2])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(offsets[-1])
+    p = np.random.default_rng(3).integers(0, K, size=T)
+    x = torch.zeros((T, K), dtype=torch.bfloat16)
+    x[np.arange(T), p] = 1.0
+    y = api.nf4_grouped_matmul_fwd(x.to(DEV), torch.from_numpy(offsets).to(DEV), wq, E)
+    got = y.cpu().view(torch.int16).numpy().view(np.uint16)
+    exp = np.repeat(np.arange(E), counts)
+    want = np.stack([wb[exp[t], :, p[t]] for t in range(T)])
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_olmoe_experts(proj):
+    """OLMoE-1B-7B experts: 512 tokens, top-8 of 64, nested NF4 stacks."""
+    E, H, I = WL.OLMOE_E, WL.OLMOE_HIDDEN, WL.OLMOE_INTER
+    N, K = (I, H) if proj == "gate" else (H, I)
+    _, _, offsets = WL.olmoe_routing()
+    T = int(offsets[-1])
+    assert T == WL.OLMOE_TOKENS * WL.OLMOE_TOPK
+    wq, wb = _stack(E, N, K, True, 10 + (proj == "down"))
+    x = WL.x_bf16(T, K, WL.W_OLMOE, 60)
+    gy = WL.grad_y_bf16(T, N, WL.W_OLMOE, 61)
+    off = torch.from_numpy(offsets).to(DEV)
+    y = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+    gx = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
+    xb, gyb, aw = WL.bf16_bits(x), WL.bf16_bits(gy), abs_bits(wb)
+    assert_close(y, O.grouped_matmul_fwd(xb, offsets, wb), f"olmoe {proj} y",
+                 O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
+    assert_close(gx, O.grouped_matmul_bwd_input(gyb, offsets, wb), f"olmoe {proj} gx",
+                 O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)
+    y2 = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
