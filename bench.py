@@ -1,0 +1,365 @@
+"""Benchmark of the fused NF4 dequantise-and-multiply path on one MI355X.
+
+A step is one pass of the hot path over the Llama-3.1-8B-shaped stack at
+batch 1, S = 512 (M = 512): for each of 32 layers and each of the 7
+projections (q, k, v, o, gate, up, down), the fused forward y = x . W^T, then
+the fused input gradient grad_x = grad_y . W (layers in reverse), all from
+nested NF4 weights resident in HBM (224 distinct weights, 3.6 GB packed).
+The metric is TFLOP/s of algorithmic work (2 M N K per GEMM) and its fraction
+of the bf16 dense MFMA peak.
+
+Prints ONE JSON line.  Secondary workloads (decode-size M over the same 224
+weights, the Qwen-32B-shaped layer at M = 2048, OLMoE grouped experts) are
+measured after the main step and reported inside the line under "extra";
+the oracle's CPU time on a bounded sample is under "cpu_baseline".
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6       # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+METRIC = "NF4 fused GEMM TFLOP/s (fwd + bwd_input) at M=512/2048; % of bf16 MFMA peak"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def clocks():
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        out = {}
+        for ln in r.stdout.splitlines():
+            low = ln.lower()
+            for key in ("sclk", "mclk", "fclk"):
+                if f"({key})" in low or f" {key} " in low:
+                    out[key] = ln.split(":")[-1].strip()
+        return out or None
+    except Exception:
+        return None
+
+
+def timed(torch, stream, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def build_stack(torch, api, WL, projs, layers, code, ncode, dev, seed0):
+    weights = []
+    for l in range(layers):
+        row = []
+        for i, p in enumerate(projs):
+            w = WL.gpu_weight_f32(p.N, p.K, seed=seed0 + l * 16 + i, device=dev)
+            row.append(api.nf4_quantize(w, code, ncode))
+            del w
+        weights.append(row)
+    torch.cuda.synchronize()
+    return weights
+
+
+def layer_inputs(torch, WL, projs, layers, M, dev, seed0):
+    """One input per producer inside a layer (q/k/v share, gate/up share), a
+    grad_y per projection."""
+    xs, gys = [], []
+    kdim = {p.name: p.K for p in projs}
+    for l in range(layers):
+        xa = WL.gpu_normal_bf16(M, kdim["q"], seed=seed0 + 4 * l, device=dev)
+        xo = WL.gpu_normal_bf16(M, kdim["o"], seed=seed0 + 4 * l + 1, device=dev)
+        xm = WL.gpu_normal_bf16(M, kdim["gate"], seed=seed0 + 4 * l + 2, device=dev)
+        xd = WL.gpu_normal_bf16(M, kdim["down"], seed=seed0 + 4 * l + 3, device=dev)
+        xs.append([xa, xa, xa, xo, xm, xm, xd])
+        gys.append([WL.gpu_normal_bf16(M, p.N, seed=seed0 + 10_000 + l * 16 + i, device=dev)
+                    for i, p in enumerate(projs)])
+    return xs, gys
+
+
+def run_stack_step(api, weights, xs, gys, ys, gxs, ws):
+    """One step: every layer's 7 fused forwards, then every layer's 7 fused
+    input gradients in reverse order."""
+    L, P = len(weights), len(weights[0])
+    for l in range(L):
+        for i in range(P):
+            api.nf4_matmul_fwd(xs[l][i], weights[l][i], out=ys[i], ws=ws)
+    for l in reversed(range(L)):
+        for i in reversed(range(P)):
+            api.nf4_matmul_bwd_input(gys[l][i], weights[l][i], out=gxs[i], ws=ws)
+
+
+def workspace_for(torch, api, projs, Ms, dev):
+    need = 16
+    for M in Ms:
+        for p in projs:
+            need = max(need, api.nf4_workspace_bytes(1, M, p.N, p.K), api.nf4_workspace_bytes(2, M, p.N, p.K))
+    return torch.empty(need, dtype=torch.uint8, device=dev)
+
+
+# ---------------------------------------------------------------------------
+def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
+    extra = {}
+    projs = WL.LLAMA_8B
+    L = len(llama_weights)
+    wbytes = sum(w.nbytes() for row in llama_weights for w in row)
+
+    # decode-size M: forward only over the same 224 weights (3.6 GB, beyond the
+    # 256 MB last-level cache)
+    dec = {}
+    for M in WL.DECODE_MS:
+        xs = [WL.gpu_normal_bf16(M, p.K, seed=40_000 + 7 * M + i, device=dev) for i, p in enumerate(projs)]
+        ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device=dev) for p in projs]
+        ws = workspace_for(torch, api, projs, [M], dev)
+
+        def one_pass():
+            for l in range(L):
+                for i in range(len(projs)):
+                    api.nf4_matmul_fwd(xs[i], llama_weights[l][i], out=ys[i], ws=ws)
+
+        ms = timed(torch, stream, one_pass, steps=5, warmup=2)
+        gbs = wbytes / (ms * 1e-3) / 1e9
+        dec[f"M={M}"] = {"us_per_pass": round(ms * 1e3, 1), "weight_GBps": round(gbs, 1),
+                         "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+        del xs, ys, ws
+    extra["decode_llama8b_fwd"] = dec
+
+    log(f"decode done: {dec}")
+    # Qwen-32B-shaped layer at M = 2048: two layer copies, rotated
+    qp = WL.QWEN_32B
+    M = WL.QWEN_M
+    qw = build_stack(torch, api, WL, qp, 2, code, ncode, dev, seed0=50_000)
+    xs, gys = layer_inputs(torch, WL, qp, 2, M, dev, seed0=60_000)
+    ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device=dev) for p in qp]
+    gxs = [torch.empty((M, p.K), dtype=torch.bfloat16, device=dev) for p in qp]
+    ws = workspace_for(torch, api, qp, [M], dev)
+    ms = timed(torch, stream, lambda: run_stack_step(api, qw, xs, gys, ys, gxs, ws), steps=3, warmup=1)
+    flops = 2 * 2 * sum(2.0 * M * p.N * p.K for p in qp)
+    # bitwise repeatability of the last layer's outputs
+    run_stack_step(api, qw, xs, gys, ys, gxs, ws)
+    y_a, g_a = ys[6].clone(), gxs[0].clone()
+    run_stack_step(api, qw, xs, gys, ys, gxs, ws)
+    same = bool(torch.equal(ys[6].view(torch.int16), y_a.view(torch.int16)) and
+                torch.equal(gxs[0].view(torch.int16), g_a.view(torch.int16)))
+    tf = flops / (ms * 1e-3) / 1e12
+    extra["qwen32b_m2048_fwd_bwd"] = {"ms_per_layer": round(ms / 2, 3), "tflops": round(tf, 1),
+                                      "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                      "bitwise_repeat": same}
+    del qw, xs, gys, ys, gxs, ws
+
+    log(f"qwen done: {extra['qwen32b_m2048_fwd_bwd']}")
+    # OLMoE grouped experts: 512 tokens, top-8 of 64; gate/up [64,1024,2048], down [64,2048,1024]
+    E, H, I = WL.OLMOE_E, WL.OLMOE_HIDDEN, WL.OLMOE_INTER
+    _, _, offsets = WL.olmoe_routing()
+    T = int(offsets[-1])
+    off = torch.from_numpy(offsets).to(dev)
+    stacks = {}
+    for j, (name, N, K) in enumerate((("gate", I, H), ("up", I, H), ("down", H, I))):
+        w = WL.gpu_weight_f32(E * N, K, seed=70_000 + j, device=dev)
+        stacks[name] = (api.nf4_quantize(w, code, ncode).per_expert(E), N, K)
+        del w
+    xin = {n: WL.gpu_normal_bf16(T, K, seed=71_000 + j, device=dev) for j, (n, (_, N, K)) in enumerate(stacks.items())}
+    gin = {n: WL.gpu_normal_bf16(T, N, seed=72_000 + j, device=dev) for j, (n, (_, N, K)) in enumerate(stacks.items())}
+    outs = {n: torch.empty((T, N), dtype=torch.bfloat16, device=dev) for n, (_, N, K) in stacks.items()}
+    gouts = {n: torch.empty((T, K), dtype=torch.bfloat16, device=dev) for n, (_, N, K) in stacks.items()}
+
+    def moe_fwd():
+        for n, (wq, N, K) in stacks.items():
+            api.nf4_grouped_matmul_fwd(xin[n], off, wq, E, out=outs[n])
+
+    def moe_bwd():
+        for n, (wq, N, K) in stacks.items():
+            api.nf4_grouped_matmul_bwd_input(gin[n], off, wq, E, out=gouts[n])
+
+    ms_f = timed(torch, stream, moe_fwd, steps=10, warmup=3)
+    ms_b = timed(torch, stream, moe_bwd, steps=10, warmup=3)
+    fl = sum(2.0 * T * N * K for (_, N, K) in stacks.values())
+    wb = sum(wq.nbytes() for (wq, _, _) in stacks.values())
+    extra["olmoe_grouped"] = {
+        "fwd_us": round(ms_f * 1e3, 1), "bwd_us": round(ms_b * 1e3, 1),
+        "fwd_tflops": round(fl / (ms_f * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(fl / (ms_b * 1e-3) / 1e12, 1),
+        "fwd_weight_GBps": round(wb / (ms_f * 1e-3) / 1e9, 1),
+        "rows": T,
+    }
+    return extra
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(WL):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    layer 0 of the Llama-3.1-8B stack at M = 512, all 7 projections, each
+    dequantised from its packed NF4 form and multiplied forward and backward
+    (the oracle's fp64 matmul).  Quantisation is set-up and not timed."""
+    import numpy as np
+    from oracle import nf4_oracle as O
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads") or 0) for d in threadpool_info()) or None
+    except Exception:
+        pass
+    projs = WL.LLAMA_8B
+    M = WL.LLAMA_M
+    code, ncode = WL.nf4_code_np(), WL.nested_code_np()
+    qs = []
+    for i, p in enumerate(projs):
+        w = WL.weight_f32(p.N, p.K, WL.W_LLAMA, 0, i)
+        qs.append(O.quantize_nf4(w, code, ncode, nested=True))
+        del w
+    x = {p.K: WL.bf16_bits(WL.x_bf16(M, p.K, WL.W_LLAMA, 0)) for p in projs}
+    gy = [WL.bf16_bits(WL.grad_y_bf16(M, p.N, WL.W_LLAMA, 0, i)) for i, p in enumerate(projs)]
+    # repeat the layer pass until at least 10 s of CPU work (at most 8 passes)
+    passes = 0
+    t0 = time.perf_counter()
+    while passes < 8 and (passes == 0 or time.perf_counter() - t0 < 10.0):
+        for i, p in enumerate(projs):
+            q = qs[i]
+            wb = O.dequantize_nf4_bf16_bits(q["packed"], q["absmax"], q["nested_absmax"],
+                                            q["nested_offset"], code, ncode).reshape(p.N, p.K)
+            O.matmul_fwd(x[p.K], wb)
+            O.matmul_bwd_input(gy[i], wb)
+        passes += 1
+    dt = time.perf_counter() - t0
+    flops = passes * 2 * sum(2.0 * M * p.N * p.K for p in projs)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"Llama-3.1-8B layer 0 (7 projections) at M=512, {passes} pass(es): dequantise "
+                      f"+ fwd + bwd_input, NumPy oracle (fp64 matmul)",
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported here.  The "
+              f"data-parallel path needs no collective (each GPU runs this step on its own rows "
+              f"of x and grad_y against a replica of the frozen packed weights).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as WL
+    from nf4_bit_weight_amd import api
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    clk_before = clocks()
+    code = torch.from_numpy(WL.nf4_code_np()).to(dev)
+    ncode = torch.from_numpy(WL.nested_code_np()).to(dev)
+
+    M, L, projs = WL.LLAMA_M, WL.LLAMA_LAYERS, WL.LLAMA_8B
+    t0 = time.time()
+    log("building the 32-layer Llama-3.1-8B NF4 stack")
+    weights = build_stack(torch, api, WL, projs, L, code, ncode, dev, seed0=10_000)
+    xs, gys = layer_inputs(torch, WL, projs, L, M, dev, seed0=20_000)
+    ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device=dev) for p in projs]
+    gxs = [torch.empty((M, p.K), dtype=torch.bfloat16, device=dev) for p in projs]
+    ws = workspace_for(torch, api, projs, [M], dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    weight_bytes = sum(w.nbytes() for row in weights for w in row)
+
+    flops_gemm = {i: 2.0 * M * p.N * p.K for i, p in enumerate(projs)}
+    flops_step = 2 * L * sum(flops_gemm.values())
+
+    log(f"stack ready in {time.time() - t0:.1f}s; timing {args.steps} steps")
+    wall0 = time.perf_counter()
+    ms_step = timed(torch, stream, lambda: run_stack_step(api, weights, xs, gys, ys, gxs, ws),
+                    args.steps, args.warmup)
+    wall = time.perf_counter() - wall0
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+
+    log(f"{ms_step:.3f} ms/step = {tflops:.1f} TFLOP/s; per-shape timing")
+    # Per-shape timing for the roofline: for each (direction, projection) the
+    # 32 launches of one step (one per layer, distinct weights) run back to
+    # back between two HIP events on the launch stream; avg = span / 32.
+    per = {}
+    for d in ("fwd", "bwd"):
+        for i, p in enumerate(projs):
+            def one(i=i, d=d):
+                for l in range(L):
+                    if d == "fwd":
+                        api.nf4_matmul_fwd(xs[l][i], weights[l][i], out=ys[i], ws=ws)
+                    else:
+                        api.nf4_matmul_bwd_input(gys[l][i], weights[l][i], out=gxs[i], ws=ws)
+            per[(d, i)] = timed(torch, stream, one, steps=3, warmup=1) / L       # ms per launch
+    per_kernel = {}
+    for (d, i), avg in sorted(per.items()):
+        per_kernel[f"{d}_{projs[i].name}"] = {"avg_us": round(avg * 1e3, 2),
+                                              "tflops": round(flops_gemm[i] / (avg * 1e-3) / 1e12, 1)}
+    dom = max(per, key=lambda k: per[k])                 # largest share of the step
+    dom_avg_s = per[dom] * 1e-3
+    achieved = flops_gemm[dom[1]] / dom_avg_s / 1e12
+    p = projs[dom[1]]
+    roofline = {
+        "bound": "mfma",
+        "kernel": f"fused NF4 {'forward' if dom[0] == 'fwd' else 'input gradient'} "
+                  f"{p.name} (M={M}, N={p.N}, K={p.K})",
+        "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        "avg_launch_us": round(dom_avg_s * 1e6, 2),
+    }
+
+    extra = {}
+    if not args.no_extra:
+        log("secondary workloads")
+        del xs, gys, ys, gxs
+        extra = run_extra(torch, api, WL, code, ncode, dev, weights, stream)
+    if not args.no_cpu:
+        log("oracle CPU baseline")
+    cpu = None if args.no_cpu else cpu_baseline(WL)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 activations, 0.02*N(0,1) weights quantised to nested NF4 on the GPU",
+        "config": {
+            "workload": "Llama-3.1-8B NF4 projections, batch 1 x S=512 (M=512), 32 layers x 7 "
+                        "projections, fused forward then fused input gradient",
+            "M": M, "layers": L, "projections": {q.name: [q.N, q.K] for q in projs},
+            "nested": True, "weight_bytes": weight_bytes,
+            "tflop_per_step": round(flops_step / 1e12, 3),
+        },
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_kernel": per_kernel,
+        "extra": extra,
+        "clocks": {"before": clk_before, "after": clocks()},
+        "setup_s": round(setup_s, 1),
+        "timed_wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,6 +70,13 @@ class NF4Weight:
         return (self.packed, self.absmax, self.nested_absmax, self.nested_offset,
                 self.code, self.nested_code)
 
+    def per_expert(self, E: int) -> "NF4Weight":
+        """View of an [E*N, K] stack quantised as one tensor, with N per expert
+        (the form the grouped calls take)."""
+        if self.N % E:
+            raise ValueError(f"{self.N} rows do not split into {E} experts")
+        return NF4Weight(*self.tensors(), self.N // E, self.K)
+
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.tensors()[:4] if t is not None)
 

@@ -7,31 +7,34 @@
 //   grouped       the same per expert over expert-sorted rows (Experts PR,
 //                 "Commit 2")
 //
-// Both directions are one "NT" contraction C[m, j] = sum_c A[m, c] * B(j, c)
-// with the contraction index contiguous in LDS for A and B:
-//   forward : A = x [M, K],       j = n, c = k, B(j, c) = W_hat[j, c]
-//   backward: A = grad_y [M, N],  j = k, c = n, B(j, c) = W_hat[c, j]
+// Both directions are one contraction C[m, j] = sum_c A[m, c] * B(c, j):
+//   forward : A = x [M, K],       j = n, c = k, B(c, j) = W_hat[j, c]
+//   backward: A = grad_y [M, N],  j = k, c = n, B(c, j) = W_hat[c, j]
 //
-// Work per workgroup (256 threads = 4 waves of 64): an output tile of BM x 256,
-// contraction in steps of 64 (one NF4 block).  Per step every thread expands
-// exactly one (row, 64-block) of W: one 16-entry byte table and eight 8-nibble
-// expansions (nf4_device.hpp), so each weight is expanded once per workgroup
-// and never written to HBM.  The expanded tile goes to LDS in the layout the
-// MFMA operand read wants:
-//   forward : [j][c]  -- the B fragment (8 consecutive c of one j) is one
-//             16-byte LDS read;
-//   backward: [c][j]  -- the row of W is written as it comes out; the B
-//             fragment (8 consecutive c = 8 W rows at one column) is gathered
-//             with eight 16-bit LDS reads.
-// A tiles are copied global -> registers -> LDS with 16-byte accesses.  Two
-// LDS buffers alternate so the global loads of step s+1 are in flight during
-// the MFMAs of step s; one barrier per step.
-//
-// The MFMA is v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32 accumulation).
-// Output is rounded once to bf16 (RNE).  When the tile count is too small to
-// fill the GPU, the contraction is split S ways; each split writes fp32
-// partials and a second kernel adds them in the fixed order s = 0..S-1.  No
-// atomics anywhere: repeated runs are bitwise identical.
+// One workgroup owns a BM x BN output tile and walks the contraction in steps
+// of BK (BK * BN = 16384: one step's weight tile is 256 (row, 64-block)
+// units).  Waves are specialised (see Tile below): per SIMD one producer wave
+// copies the activation tile global -> LDS with global_load_lds_dwordx4 (no
+// VGPR staging; 16-byte units of each row XOR-swizzled, swz below) and
+// expands one (row, 64-block) weight unit per thread -- one byte table, eight
+// 8-nibble expansions (nf4_device.hpp) -- straight into the LDS tile the MFMA
+// operand is read from; C consumer waves per SIMD read fragments from LDS and
+// run v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Each weight is
+// expanded once per workgroup and never written to HBM.  LDS is double
+// buffered: the producers fill step s+1 while the consumers multiply step s.
+// Weight tile layout in LDS:
+//   forward : [BN rows n][BK k], same 16-byte XOR swizzle as A; the B
+//             fragment (8 consecutive k of one n) is one 16-byte read;
+//   backward: [BK rows n][BN k + 16 pad]; the B fragment (8 consecutive n at
+//             one k) comes from two ds_read_b64_tr_b16 transposing reads
+//             (each gives a lane 4 consecutive rows of its column).
+// Output is rounded once to bf16 (RNE).  When too few tiles exist to fill the
+// GPU the contraction is split S ways; each split writes fp32 partials and a
+// second kernel adds them in the fixed order s = 0..S-1.  No atomics:
+// repeated runs are bitwise identical.
+#include <cstdlib>
+#include <type_traits>
+
 #include "nf4_device.hpp"
 #include "nf4_internal.hpp"
 
@@ -39,11 +42,11 @@ namespace nf4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;                 // contraction step = one NF4 block
-constexpr int BN = 256;                // output columns per workgroup
-constexpr int kAPitch = BK + 8;        // A tile row pitch (elements): 144 B rows
-constexpr int kBFPitch = BK + 8;       // forward B tile [j][c] pitch
-constexpr int kBTPitch = BN + 4;       // backward B tile [c][j] pitch: 520 B rows
+constexpr int kMaxBN = 256;            // widest output tile
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 struct GemmParams {
   const uint16_t* A;        // [rows, Kc] bf16
@@ -56,40 +59,68 @@ struct GemmParams {
   int32_t splits;
 };
 
-template <int BM, bool TRANS>
+// BM x BN output tile, contraction step BK chosen so the weight tile holds
+// exactly 256 (row, 64-block) units.  The workgroup has 4 producer waves and
+// 4*C consumer waves (C = 1 or 2), i.e. per SIMD one producer and C
+// consumers:
+//   producer : copies the activation tile (global -> LDS), fetches the packed
+//              weights two steps ahead and expands one (row, 64-block) unit
+//              per thread into the LDS weight tile -- pure VALU / memory work;
+//   consumer : reads MFMA fragments from LDS and issues the MFMAs of its
+//              (BM / CW_M) x (BN / CW_N) part of the tile.
+// A wave cannot issue VALU work while its own MFMA runs (measured: MFMA + 8
+// VALU ops cost ~54 cycles instead of 32), but the SIMD issues one wave's
+// VALU and another wave's MFMA in the same cycles, so splitting the roles
+// makes a step cost ~max(expansion, MFMA) instead of their sum.
+template <int BM, int BN_, bool TRANS, int C_>
 struct Tile {
-  static constexpr int kWavesM = (BM >= 128) ? 2 : 1;
-  static constexpr int kWavesN = 4 / kWavesM;
-  static constexpr int WM = BM / kWavesM;
-  static constexpr int WN = BN / kWavesN;
+  static constexpr int BN = BN_;
+  static constexpr int C = C_;
+  static constexpr int kThreads = 64 * (4 + 4 * C);
+  static constexpr int BK = 16384 / BN;             // 64 (BN 256) or 128 (BN 128)
+  static constexpr int CW_M = 2;                    // consumer waves: 2 x (2C)
+  static constexpr int CW_N = 2 * C;
+  static constexpr int WM = BM / CW_M;
+  static constexpr int WN = BN / CW_N;
   static constexpr int MI = WM / 32;
   static constexpr int NI = WN / 32;
-  static constexpr int kAChunks = BM * (BK / 8) / kThreads;     // 16-byte chunks per thread
-  static constexpr int kAElems = BM * kAPitch;
-  static constexpr int kBElems = TRANS ? BK * kBTPitch : BN * kBFPitch;
+  static constexpr int KK = BK / 16;                // MFMA k-steps per step
+  static constexpr int kUnits = BK / 8;             // 16-byte units per tile row
+  static constexpr int kARowsPerInstr = 64 / kUnits;
+  static constexpr int kARowsPerWave = BM / 4;      // activation rows per producer wave
+  static constexpr int kBTPitch = BN + 16;          // backward weight tile pitch (elements)
+  static constexpr int kAElems = BM * BK;
+  static constexpr int kBElems = TRANS ? BK * kBTPitch : BN * BK;
   static constexpr int kLdsBytes = 2 * (kAElems + kBElems) * 2;
-  static_assert(kAChunks >= 1, "tile too small");
-  static_assert(MI >= 1 && NI >= 1, "bad wave tile");
+  static_assert(MI >= 1 && NI >= 1, "tile too small");
+  static_assert(kARowsPerWave % kARowsPerInstr == 0, "A copy split");
+  static_assert(kLdsBytes + 1024 <= 160 * 1024, "LDS budget of one workgroup");
 };
 
-template <int BM, bool TRANS, bool NESTED, bool GROUPED>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmParams p) {
-  using T = Tile<BM, TRANS>;
+// 16-byte unit u of row r of a [rows][BK] tile is stored at unit u ^ ((r >> 1) & 7):
+// for the MFMA fragment reads (32 rows x 2 units per wave instruction) this
+// measured ~1.4x the LDS throughput of u ^ (r & 7) on gfx950.
+__device__ __forceinline__ int swz(int r, int u) { return u ^ ((r >> 1) & 7); }
+
+template <int BM, int BN, bool TRANS, bool NESTED, bool GROUPED, int C>
+__global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
+  using T = Tile<BM, BN, TRANS, C>;
+  constexpr int BK = T::BK;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ float sncode[256];
 
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int64_t N = p.w.N, K = p.w.K;
   const int64_t Nc = TRANS ? K : N;        // output columns
   const int64_t Kc = TRANS ? N : K;        // contraction length
   const int ktiles = static_cast<int>((Kc + BK - 1) / BK);
 
-  // ---- which rows does this workgroup own --------------------------------
+  // ---- rows owned by this workgroup ---------------------------------------
   int64_t row0, row_end, wrow_base = 0;
   if constexpr (GROUPED) {
     const int mt = blockIdx.y;
-    int acc = 0;
-    int e_found = -1;
+    int acc = 0, e_found = -1;
     int64_t lo = 0, hi = 0;
     for (int e = 0; e < p.E; ++e) {
       int64_t a = p.offsets[e], b = p.offsets[e + 1];
@@ -109,110 +140,155 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmParams p) {
   }
   const int64_t col0 = static_cast<int64_t>(blockIdx.x) * BN;
   const int z = blockIdx.z;
-  const int kt_begin = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
-  const int kt_end = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
+  const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
+  const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
 
-  float code[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
-  float off = 0.f;
-  if constexpr (NESTED) {
-    sncode[tid] = p.w.ncode[tid];
-    off = p.w.nested_offset[0];
-  }
-
-  // LDS: A buffers 0/1, then B buffers 0/1
   auto a_tile = [&](int buf) { return lds + buf * T::kAElems; };
   auto b_tile = [&](int buf) { return lds + 2 * T::kAElems + buf * T::kBElems; };
 
-  // ---- per-thread roles for the copies ------------------------------------
-  // A: chunk c = tid + 256*i -> row c/8, 16-byte column c%8
-  // B: forward  -> W row (col0 + tid), block kt
-  //    backward -> W row (kt*64 + tid/4), column block (col0/64 + tid%4)
-  u32x4_t areg[T::kAChunks];
-  u32x4_t breg[2];
-  uint32_t sraw = 0;      // u8 nested index or fp32 bits of the plain absmax
-  float s2 = 0.f;
-  bool bvalid = false;
-
-  auto load_tiles = [&](int kt) {
-    const int64_t c0 = static_cast<int64_t>(kt) * BK;
+  if (wave < 4) {
+    // =================== producer waves (threads 0..255) ======================
+    float code[16];
 #pragma unroll
-    for (int i = 0; i < T::kAChunks; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c >> 3, cc = (c & 7) * 8;
-      const int64_t row = row0 + r;
-      if (row < row_end && c0 + cc < Kc) {
-        areg[i] = *reinterpret_cast<const u32x4_t*>(p.A + row * Kc + c0 + cc);
-      } else {
-        areg[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
+    float off = 0.f;
+    if constexpr (NESTED) {
+      sncode[tid] = p.w.ncode[tid];
+      off = p.w.nested_offset[0];
+    }
+
+    // Activation tile: global -> LDS directly.  Producer wave w copies rows
+    // [w*BM/4, (w+1)*BM/4), 1 KB per instruction; lane l fills physical unit
+    // l%U of row l/U (U = BK/8 units per row) with logical unit swz(row, l%U).
+    // Rows past the end are clamped to the last valid row (their products
+    // are never stored); contraction columns past Kc are clamped inside the
+    // row and meet zero weights.
+    const int a_r_in = lane / T::kUnits;
+    const int a_unit = lane % T::kUnits;
+    auto issue_a = [&](int kt, int buf) {
+      const int64_t c0 = static_cast<int64_t>(kt) * BK;
+#pragma unroll
+      for (int i = 0; i < T::kARowsPerWave / T::kARowsPerInstr; ++i) {
+        const int r = wave * T::kARowsPerWave + i * T::kARowsPerInstr + a_r_in;
+        int64_t row = row0 + r;
+        row = row < row_end ? row : row_end - 1;
+        int64_t col = c0 + 8 * swz(r, a_unit);
+        col = col < Kc ? col : Kc - 8;
+        const uint16_t* src = p.A + row * Kc + col;
+        uint16_t* dst = a_tile(buf) + (wave * T::kARowsPerWave + i * T::kARowsPerInstr) * BK;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
       }
-    }
-    int64_t wrow, wcol;
-    if constexpr (TRANS) {
-      wrow = c0 + (tid >> 2);
-      wcol = col0 + 64 * (tid & 3);
-      bvalid = (wrow < N) && (wcol < K);
-    } else {
-      wrow = col0 + tid;
-      wcol = c0;
-      bvalid = wrow < N;
-    }
-    if (bvalid) {
-      const int64_t flat = (wrow_base + wrow) * K + wcol;       // multiple of 64
+    };
+
+    // Weight tile units, fetched two steps ahead into registers:
+    //   forward : thread t expands W row (col0 + t % BN), block (kt*BK/64 + t / BN)
+    //   backward: thread t expands W row (kt*BK + t % BK), block (col0/64 + t / BK)
+    // Out-of-range rows or columns load a valid address and are then replaced
+    // by all-7 nibbles (code 0) with scale 0, so the expansion writes zeros
+    // without a branch.
+    struct BRaw {
+      u32x4_t pk[2];
+      uint32_t sraw;    // u8 nested index or fp32 bits of the plain absmax
+      float s2;
+      bool valid;
+    };
+    auto load_b = [&](int kt, BRaw& r) {
+      const int64_t c0 = static_cast<int64_t>(kt) * BK;
+      int64_t wrow, wcol;
+      if constexpr (TRANS) {
+        wrow = c0 + (tid % BK);
+        wcol = col0 + 64 * (tid / BK);
+      } else {
+        wrow = col0 + (tid % BN);
+        wcol = c0 + 64 * (tid / BN);
+      }
+      r.valid = (wrow < N) && (wcol < K);
+      const int64_t flat = r.valid ? (wrow_base + wrow) * K + wcol : 0;   // multiple of 64
       const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + flat / 2);
-      breg[0] = src[0];
-      breg[1] = src[1];
+      r.pk[0] = src[0];
+      r.pk[1] = src[1];
       const int64_t b = flat / kBlock;
       if constexpr (NESTED) {
-        sraw = static_cast<const uint8_t*>(p.w.absmax)[b];
-        s2 = p.w.nested_absmax[b / kNestedBlock];
+        r.sraw = static_cast<const uint8_t*>(p.w.absmax)[b];
+        r.s2 = p.w.nested_absmax[b / kNestedBlock];
       } else {
-        sraw = __float_as_uint(static_cast<const float*>(p.w.absmax)[b]);
+        r.sraw = __float_as_uint(static_cast<const float*>(p.w.absmax)[b]);
       }
-    }
-  };
-
-  auto store_tiles = [&](int buf) {
-    uint16_t* a_s = a_tile(buf);
-#pragma unroll
-    for (int i = 0; i < T::kAChunks; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c >> 3, cc = (c & 7) * 8;
-      *reinterpret_cast<u32x4_t*>(a_s + r * kAPitch + cc) = areg[i];
-    }
-    uint32_t o[8][4];
-    if (bvalid) {
+    };
+    auto b_dst = [&](int buf, int d) -> uint16_t* {
+      if constexpr (TRANS) {
+        return b_tile(buf) + (tid % BK) * T::kBTPitch + 64 * (tid / BK) + 8 * d;
+      } else {
+        const int row = tid % BN;
+        return b_tile(buf) + row * BK + 8 * swz(row, 8 * (tid / BN) + d);
+      }
+    };
+    auto expand_into = [&](const BRaw& r, int buf) {
       float a;
-      if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[sraw], s2), off);
-      else a = __uint_as_float(sraw);
-      const Lut t = make_lut(code, a);
-#pragma unroll
-      for (int d = 0; d < 8; ++d) expand8(breg[d >> 2][d & 3], t, o[d]);
-    } else {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[d][0] = o[d][1] = o[d][2] = o[d][3] = 0u;
-    }
-    uint16_t* b_s = b_tile(buf);
-    if constexpr (TRANS) {
-      uint16_t* dst = b_s + (tid >> 2) * kBTPitch + 64 * (tid & 3);   // 8-byte aligned
+      if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[r.sraw], r.s2), off);
+      else a = __uint_as_float(r.sraw);
+      const u32x4_t zero_codes = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+      const u32x4_t pk0 = r.valid ? r.pk[0] : zero_codes;
+      const u32x4_t pk1 = r.valid ? r.pk[1] : zero_codes;
+      const Lut t = make_lut(code, r.valid ? a : 0.f);
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        reinterpret_cast<u32x2_t*>(dst + 8 * d)[0] = u32x2_t{o[d][0], o[d][1]};
-        reinterpret_cast<u32x2_t*>(dst + 8 * d)[1] = u32x2_t{o[d][2], o[d][3]};
+        uint32_t o[4];
+        expand8(d < 4 ? pk0[d] : pk1[d - 4], t, o);
+        *reinterpret_cast<u32x4_t*>(b_dst(buf, d)) = u32x4_t{o[0], o[1], o[2], o[3]};
       }
-    } else {
-      uint16_t* dst = b_s + tid * kBFPitch;                          // 16-byte aligned
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-        *reinterpret_cast<u32x4_t*>(dst + 8 * d) = u32x4_t{o[d][0], o[d][1], o[d][2], o[d][3]};
-    }
-  };
+    };
+    // End of a step: the activation copy issued this step has landed
+    // (vector-memory operations complete in issue order, so vmcnt(kWLoads)
+    // leaves only the weight loads in flight) and the expansion's LDS writes
+    // are done; then the workgroup barrier.
+    constexpr int kWLoads = NESTED ? 4 : 3;          // dwordx4 x2 + scale load(s)
+    auto end_step = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt((kWLoads & 15) | (7 << 4));   // vmcnt(kWLoads) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
 
-  // ---- MFMA roles ---------------------------------------------------------
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave / T::kWavesN, wn = wave % T::kWavesN;
-  const int r = lane & 31, h = lane >> 5;
+    if (kb < ke) {
+      if constexpr (NESTED) __syncthreads();      // sncode filled (matched by consumers)
+      BRaw r0, r1;
+      issue_a(kb, 0);
+      load_b(kb, r0);
+      load_b(kb + 1 < ke ? kb + 1 : kb, r1);
+      expand_into(r0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      // invariant at the top: buffer 0 holds step s, r1 holds step s+1
+      int s = kb;
+      for (; s + 2 < ke; s += 2) {
+        issue_a(s + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(s + 2, r0);
+        expand_into(r1, 1);
+        end_step();
+        issue_a(s + 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(s + 3 < ke ? s + 3 : s + 2, r1);
+        expand_into(r0, 0);
+        end_step();
+      }
+      if (s + 1 < ke) {
+        issue_a(s + 1, 1);
+        expand_into(r1, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
+  // ===================== consumer waves ========================================
+  const int cw = wave - 4;
+  const int wm = cw / T::CW_N, wn = cw % T::CW_N;
+  const int r32 = lane & 31, h = lane >> 5;
   f32x16_t acc[T::MI][T::NI];
 #pragma unroll
   for (int i = 0; i < T::MI; ++i)
@@ -221,61 +297,93 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](int buf) {
+  // fragment addresses (elements) that do not depend on the step
+  int a_row[T::MI];
+#pragma unroll
+  for (int i = 0; i < T::MI; ++i) a_row[i] = wm * T::WM + 32 * i + r32;
+  // backward transposing read: lane l of 16-lane group g, index s = l%16
+  const int tg = lane >> 4, ts = lane & 15;
+  const int tr_row = 8 * (tg >> 1) + (ts >> 2);                     // + 16*kk + 4*half
+  const int tr_col = wn * T::WN + 16 * (tg & 1) + 4 * (ts & 3);     // + 32*j
+
+  struct Frags {
+    bf16x8_t a[T::MI];
+    bf16x8_t b[T::NI];
+  };
+  auto load_frags = [&](int buf, int kk, Frags& f) {
     const uint16_t* a_s = a_tile(buf);
+#pragma unroll
+    for (int i = 0; i < T::MI; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8_t*>(a_s + a_row[i] * BK + 8 * swz(a_row[i], 2 * kk + h));
     const uint16_t* b_s = b_tile(buf);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[T::MI], bfr[T::NI];
-#pragma unroll
-      for (int i = 0; i < T::MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(a_s + (wm * T::WM + 32 * i + r) * kAPitch + 16 * kk + 8 * h);
-#pragma unroll
-      for (int j = 0; j < T::NI; ++j) {
-        if constexpr (TRANS) {
-          const uint16_t* src = b_s + (16 * kk + 8 * h) * kBTPitch + wn * T::WN + 32 * j + r;
-          uint32_t u[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            u[e] = static_cast<uint32_t>(src[(2 * e) * kBTPitch]) |
-                   (static_cast<uint32_t>(src[(2 * e + 1) * kBTPitch]) << 16);
-          bfr[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{u[0], u[1], u[2], u[3]});
-        } else {
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(b_s + (wn * T::WN + 32 * j + r) * kBFPitch + 16 * kk + 8 * h);
-        }
+    for (int j = 0; j < T::NI; ++j) {
+      if constexpr (TRANS) {
+        const uint16_t* src = b_s + (16 * kk + tr_row) * T::kBTPitch + tr_col + 32 * j;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * T::kBTPitch));
+        u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
+        f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
+      } else {
+        const int brow = wn * T::WN + 32 * j + r32;
+        f.b[j] = *reinterpret_cast<const bf16x8_t*>(b_s + brow * BK + 8 * swz(brow, 2 * kk + h));
       }
+    }
+  };
+  // Fragments of k-step kk+1 are read while the MFMAs of kk run; the
+  // scheduling fence per k-step keeps the compiler from hoisting every
+  // step's reads ahead (two fragment sets live at most).
+  auto compute = [&](int buf) {
+    Frags f0, f1;
+    load_frags(buf, 0, f0);
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk) {
+      Frags& fc = (kk & 1) ? f1 : f0;
+      Frags& fn = (kk & 1) ? f0 : f1;
+      if (kk + 1 < T::KK) load_frags(buf, kk + 1, fn);
 #pragma unroll
       for (int i = 0; i < T::MI; ++i)
 #pragma unroll
         for (int j = 0; j < T::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto end_step = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // ---- main loop ------------------------------------------------------------
-  if (kt_begin < kt_end) {
-    if constexpr (NESTED) __syncthreads();       // sncode visible
-    load_tiles(kt_begin);
-    store_tiles(0);
-    __syncthreads();
-    int buf = 0;
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const bool more = kt + 1 < kt_end;
-      if (more) load_tiles(kt + 1);
-      compute(buf);
-      if (more) store_tiles(buf ^ 1);
+  if (kb < ke) {
+    if constexpr (NESTED) __syncthreads();        // matches the producers' sncode barrier
+    __syncthreads();                              // step kb is in buffer 0
+    int s = kb;
+    for (; s + 2 < ke; s += 2) {
+      compute(0);
+      end_step();
+      compute(1);
+      end_step();
+    }
+    if (s + 1 < ke) {
+      compute(0);
       __syncthreads();
-      buf ^= 1;
+      compute(1);
+    } else {
+      compute(0);
     }
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  // acc[i][j][v] holds C[32i + 8(v/4) + 4h + v%4][32j + r] of the wave tile.
+  // ---- epilogue ----------------------------------------------------------------
+  // acc[i][j][v] holds C[32i + 8(v/4) + 4h + v%4][32j + r32] of the wave tile.
 #pragma unroll
   for (int i = 0; i < T::MI; ++i) {
 #pragma unroll
     for (int j = 0; j < T::NI; ++j) {
-      const int64_t col = col0 + wn * T::WN + 32 * j + r;
+      const int64_t col = col0 + wn * T::WN + 32 * j + r32;
       if (col >= Nc) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -292,20 +400,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmParams p) {
 }
 
 // Fixed-order sum of split partials: out = bf16(sum_{s=0}^{S-1} part[s]).
+// Four outputs per thread; n % 4 tails handled one by one.
 __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restrict__ part,
                                                             int splits, int64_t n,
                                                             uint16_t* __restrict__ out) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= n) return;
-  float s = part[i];
-  for (int z = 1; z < splits; ++z) s = __fadd_rn(s, part[static_cast<int64_t>(z) * n + i]);
-  out[i] = to_bf16(s);
+  const int64_t i4 = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  if (i4 + 4 <= n && (n & 3) == 0) {
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(part + i4);
+    for (int z = 1; z < splits; ++z) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + static_cast<int64_t>(z) * n + i4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = __fadd_rn(s[e], v[e]);
+    }
+    const uint32_t lo = pack_bf16x2(s[0], s[1]), hi = pack_bf16x2(s[2], s[3]);
+    *reinterpret_cast<u32x2_t*>(out + i4) = u32x2_t{lo, hi};
+  } else {
+    for (int64_t i = i4; i < n && i < i4 + 4; ++i) {
+      float s = part[i];
+      for (int z = 1; z < splits; ++z) s = __fadd_rn(s, part[static_cast<int64_t>(z) * n + i]);
+      out[i] = to_bf16(s);
+    }
+  }
 }
 
-template <int BM, bool TRANS, bool NESTED, bool GROUPED>
+template <int BM, int BN, bool TRANS, bool NESTED, bool GROUPED, int C>
 hipError_t launch_tiled(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
-  using T = Tile<BM, TRANS>;
-  auto kern = k_gemm<BM, TRANS, NESTED, GROUPED>;
+  using T = Tile<BM, BN, TRANS, C>;
+  auto kern = k_gemm<BM, BN, TRANS, NESTED, GROUPED, C>;
   // raise the dynamic-LDS limit once per template instance (thread-safe
   // static initialisation); a failure here surfaces at the launch below
   static const bool attr_done = [&] {
@@ -317,24 +439,32 @@ hipError_t launch_tiled(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hi
   (void)attr_done;
   dim3 grid(static_cast<unsigned>((n_cols + BN - 1) / BN), static_cast<unsigned>(m_tiles),
             static_cast<unsigned>(p.splits));
-  kern<<<grid, kThreads, T::kLdsBytes, stream>>>(p);
+  kern<<<grid, T::kThreads, T::kLdsBytes, stream>>>(p);
   return hipGetLastError();
 }
 
 template <bool TRANS, bool GROUPED>
-hipError_t dispatch_bm(int bm, const GemmParams& p, int64_t m_tiles, int64_t n_cols,
-                       hipStream_t stream) {
+hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_tiles,
+                         int64_t n_cols, hipStream_t stream) {
   const bool nested = p.w.nested();
-#define NF4_CASE(BMV)                                                                     \
-  if (bm == BMV) {                                                                        \
-    return nested ? launch_tiled<BMV, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)   \
-                  : launch_tiled<BMV, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream); \
+#define NF4_CASE(BMV, BNV, CV)                                                                       \
+  if (bm == BMV && bn == BNV && c == CV) {                                                           \
+    return nested ? launch_tiled<BMV, BNV, TRANS, true, GROUPED, CV>(p, m_tiles, n_cols, stream)     \
+                  : launch_tiled<BMV, BNV, TRANS, false, GROUPED, CV>(p, m_tiles, n_cols, stream);   \
   }
-  NF4_CASE(256)
-  NF4_CASE(128)
-  NF4_CASE(64)
+  NF4_CASE(256, 256, 2)
+  NF4_CASE(128, 256, 1)
+  NF4_CASE(128, 256, 2)
+  NF4_CASE(64, 256, 1)
+  NF4_CASE(128, 128, 1)
+  NF4_CASE(64, 128, 1)
 #undef NF4_CASE
   return hipErrorInvalidValue;
+}
+
+int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
 }
 
 }  // namespace
@@ -359,12 +489,23 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t kc = (kind == GemmKind::kFwd) ? K : N;
   pl.small_m = false;
   pl.bm = (M <= 64) ? 64 : (M <= 128 ? 128 : 256);
-  const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + BN - 1) / BN);
-  const int64_t ktiles = (kc + BK - 1) / BK;
+  pl.bn = 256;
+  // Tuning overrides (documented): NF4_BM, NF4_BN, NF4_CONSUMERS, NF4_SPLITS.
+  const int o_bm = env_int("NF4_BM"), o_bn = env_int("NF4_BN"), o_s = env_int("NF4_SPLITS");
+  const int o_c = env_int("NF4_CONSUMERS");
+  if (o_bm == 64 || o_bm == 128 || o_bm == 256) pl.bm = o_bm;
+  if (o_bn == 128 || o_bn == 256) pl.bn = o_bn;
+  if (pl.bm == 256) pl.bn = 256;                   // 256 x 128 at BK 128 exceeds the LDS
+  pl.consumers = (pl.bm == 256) ? 2 : 1;           // 256-row tiles: 8 consumer waves
+  if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
+  const int bk = 16384 / pl.bn;
+  const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + pl.bn - 1) / pl.bn);
+  const int64_t ksteps = (kc + bk - 1) / bk;
   int s = 1;
-  // double the split while the grid is under one workgroup per CU and every
-  // split keeps at least 4 contraction steps
-  while (tiles * s < cus && ktiles / (2 * s) >= 4 && s < 16) s *= 2;
+  // Split the contraction only while fewer than half the compute units have a
+  // tile, keeping at least 512 of the contraction per split.
+  while (tiles * s * 2 <= cus && (ksteps * bk) / (2 * s) >= 512 && s < 8) s *= 2;
+  if (o_s >= 1 && o_s <= 16) s = o_s;
   pl.splits = s;
   pl.ws_bytes = (s > 1) ? static_cast<size_t>(s) * static_cast<size_t>(M) * static_cast<size_t>(nc) * 4 : 0;
   return pl;
@@ -375,9 +516,11 @@ GemmPlan plan_grouped(GemmKind, int64_t total_M, int64_t, int64_t, int32_t E) {
   pl.small_m = false;
   pl.splits = 1;
   pl.ws_bytes = 0;
+  pl.bn = 256;
   // rows per expert are only known on the device; size the tile by the mean
   const int64_t mean = (E > 0) ? (total_M + E - 1) / E : total_M;
   pl.bm = (mean <= 96) ? 64 : (mean <= 192 ? 128 : 256);
+  pl.consumers = (pl.bm == 256) ? 2 : 1;
   return pl;
 }
 
@@ -395,13 +538,14 @@ hipError_t launch_gemm(GemmKind kind, const GemmPlan& plan, const void* A, int64
   p.E = 1;
   p.splits = plan.splits;
   const int64_t m_tiles = (M + plan.bm - 1) / plan.bm;
-  hipError_t e = trans ? dispatch_bm<true, false>(plan.bm, p, m_tiles, nc, stream)
-                       : dispatch_bm<false, false>(plan.bm, p, m_tiles, nc, stream);
+  hipError_t e = trans ? dispatch_tile<true, false>(plan.bm, plan.bn, plan.consumers, p, m_tiles, nc, stream)
+                       : dispatch_tile<false, false>(plan.bm, plan.bn, plan.consumers, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 4 : 2);
   if (plan.splits > 1) {
     const int64_t n = M * nc;
-    k_splitk_reduce<<<static_cast<unsigned>((n + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+    const int64_t threads = (n + 3) / 4;
+    k_splitk_reduce<<<static_cast<unsigned>((threads + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
         static_cast<const float*>(ws), plan.splits, n, static_cast<uint16_t*>(C));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -426,8 +570,8 @@ hipError_t launch_grouped(GemmKind kind, const GemmPlan& plan, const void* A,
   p.splits = 1;
   // upper bound on sum_e ceil(M_e / bm); workgroups past the real count exit
   const int64_t m_tiles = (total_M + plan.bm - 1) / plan.bm + E;
-  hipError_t e = trans ? dispatch_bm<true, true>(plan.bm, p, m_tiles, nc, stream)
-                       : dispatch_bm<false, true>(plan.bm, p, m_tiles, nc, stream);
+  hipError_t e = trans ? dispatch_tile<true, true>(plan.bm, plan.bn, plan.consumers, p, m_tiles, nc, stream)
+                       : dispatch_tile<false, true>(plan.bm, plan.bn, plan.consumers, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 7 : 6);
   return hipSuccess;

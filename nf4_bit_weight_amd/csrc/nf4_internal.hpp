@@ -36,6 +36,8 @@ enum class GemmKind { kFwd, kBwdInput };
 // of (M, N, K, kind, compute units).
 struct GemmPlan {
   int bm;          // rows of the activation tile
+  int bn;          // output columns per tile (256 or 128)
+  int consumers;   // MFMA waves per SIMD (1 or 2) beside one expanding wave
   int splits;      // contraction split count (1 = none)
   bool small_m;    // weight-streaming forward
   size_t ws_bytes; // fp32 partials when splits > 1

@@ -10,6 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import workloads as WL
 from nf4_bit_weight_amd.api import NF4Weight
 from oracle import nf4_oracle as O
 
@@ -31,8 +32,9 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 
 def code_tensors(nested: bool):
-    code = to_dev(O.nf4_code())
-    ncode = to_dev(O.uniform_nested_code()) if nested else None
+    """The code tables are call inputs; both sides take them from workloads."""
+    code = to_dev(WL.nf4_code_np())
+    ncode = to_dev(WL.nested_code_np()) if nested else None
     return code, ncode
 
 

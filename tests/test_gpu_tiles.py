@@ -1,0 +1,68 @@
+"""Every tile variant of the fused kernels, forced through the planner's
+documented tuning overrides (NF4_BM, NF4_BN, NF4_CONSUMERS, NF4_SPLITS), against the oracle:
+bit-exact identity probes and tolerance on ragged shapes, split and unsplit."""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from nf4_bit_weight_amd import api
+from oracle import nf4_oracle as O
+
+from gpu_util import DEV, abs_bits, assert_close, bits_of, ref_bits, upload
+
+pytestmark = pytest.mark.gpu
+
+# (rows, columns, MFMA waves per SIMD beside the expanding wave)
+TILES = [(256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1), (128, 128, 1), (64, 128, 1)]
+
+
+@pytest.fixture
+def plan_override():
+    saved = {k: os.environ.get(k) for k in ("NF4_BM", "NF4_BN", "NF4_SPLITS", "NF4_CONSUMERS")}
+
+    def set_(bm, bn, consumers, splits=0):
+        os.environ["NF4_BM"], os.environ["NF4_BN"] = str(bm), str(bn)
+        os.environ["NF4_SPLITS"], os.environ["NF4_CONSUMERS"] = str(splits), str(consumers)
+
+    yield set_
+    for k, v in saved.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+@pytest.mark.parametrize("bm,bn,consumers", TILES)
+def test_tile_identity(bm, bn, consumers, plan_override):
+    plan_override(bm, bn, consumers)
+    N, K = 320, 384
+    w = WL.weight_f32(N, K, WL.W_TINY, 500 + bm + bn)
+    ref = O.quantize_nf4(w, nested=True)
+    wq = upload(ref, N, K, True)
+    wb = ref_bits(ref, (N, K))
+    y = api.nf4_matmul_fwd(torch.eye(K, dtype=torch.bfloat16, device=DEV), wq)
+    assert np.array_equal(bits_of(y), wb.T)
+    gx = api.nf4_matmul_bwd_input(torch.eye(N, dtype=torch.bfloat16, device=DEV), wq)
+    assert np.array_equal(bits_of(gx), wb)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("bm,bn,consumers", TILES)
+@pytest.mark.parametrize("M,N,K", [(200, 392, 704), (513, 136, 1088)])
+def test_tile_vs_oracle(M, N, K, bm, bn, consumers, splits, plan_override):
+    plan_override(bm, bn, consumers, splits)
+    w = WL.weight_f32(N, K, WL.W_TINY, 600 + M)
+    ref = O.quantize_nf4(w, nested=(M % 2 == 0))
+    wq = upload(ref, N, K, M % 2 == 0)
+    wb = ref_bits(ref, (N, K))
+    x = WL.x_bf16(M, K, WL.W_TINY, 601)
+    gy = WL.grad_y_bf16(M, N, WL.W_TINY, 602)
+    xb, gyb, aw = WL.bf16_bits(x), WL.bf16_bits(gy), abs_bits(wb)
+    y = api.nf4_matmul_fwd(x.to(DEV), wq)
+    assert_close(y, O.matmul_fwd(xb, wb), "y", O.matmul_fwd(abs_bits(xb), aw), K)
+    gx = api.nf4_matmul_bwd_input(gy.to(DEV), wq)
+    assert_close(gx, O.matmul_bwd_input(gyb, wb), "grad_x", O.matmul_bwd_input(abs_bits(gyb), aw), N)

@@ -40,6 +40,12 @@ def test_code_table_matches_normalfloat_construction():
     assert np.abs(v - code).max() <= 5e-5 + 1e-7
 
 
+def test_input_tables_are_the_oracle_defaults():
+    """The tables every GPU call receives (inputs) equal the oracle's defaults."""
+    assert np.array_equal(WL.nf4_code_np(), O.nf4_code())
+    assert np.array_equal(WL.nested_code_np(), O.uniform_nested_code())
+
+
 def test_nested_table_closed_form():
     c = O.uniform_nested_code().astype(np.float64)
     assert c.shape == (256,)

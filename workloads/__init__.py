@@ -59,6 +59,24 @@ OLMOE_E, OLMOE_HIDDEN, OLMOE_INTER, OLMOE_TOPK, OLMOE_TOKENS = 64, 2048, 1024, 8
 TINY_M, TINY_N, TINY_K = 64, 128, 256
 
 
+# Call arguments, not arithmetic: the 16 NF4 levels (4-decimal NormalFloat-4
+# values) and the 256-entry nested table (2j - 255) / 255 that every call of
+# the codec and the matmuls receives as input.
+NF4_LEVELS = (
+    -1.0, -0.6962, -0.5251, -0.3949, -0.2844, -0.1848, -0.0911, 0.0,
+    0.0796, 0.1609, 0.2461, 0.3379, 0.4407, 0.5626, 0.7230, 1.0,
+)
+NESTED_UNIFORM = tuple((2.0 * j - 255.0) / 255.0 for j in range(256))
+
+
+def nf4_code_np() -> np.ndarray:
+    return np.array(NF4_LEVELS, dtype=np.float64).astype(np.float32)
+
+
+def nested_code_np() -> np.ndarray:
+    return np.array(NESTED_UNIFORM, dtype=np.float64).astype(np.float32)
+
+
 def rng(*key: int) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([BASE_SEED, *key]))
 
