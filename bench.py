@@ -42,7 +42,17 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", default=None, metavar="DIR_PROJ",
+                    help="time one shape of the step (e.g. fwd_gate: the 32 layers' forward gate "
+                         "projections) and nothing else; used for profiling")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --only: then run one plain device copy of this many bytes "
+                         "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
+
+
+def traffic_file(direction, proj, M):
+    return os.path.join(ROOT, "profiles", f"traffic_fused_gemm_{direction}_{proj}_m{M}.md")
 
 
 def clocks():
@@ -255,6 +265,51 @@ def cpu_baseline(WL):
 
 
 # ---------------------------------------------------------------------------
+def run_only(args):
+    """One shape of the step: the 32 layers' launches of one projection in one
+    direction (distinct weights, as in the step), `steps` times."""
+    import torch
+
+    import workloads as WL
+    from nf4_bit_weight_amd import api
+
+    d, name = args.only.split("_", 1)
+    projs = WL.LLAMA_8B
+    i = [p.name for p in projs].index(name)
+    p = projs[i]
+    M, L = WL.LLAMA_M, WL.LLAMA_LAYERS
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    code = torch.from_numpy(WL.nf4_code_np()).to(dev)
+    ncode = torch.from_numpy(WL.nested_code_np()).to(dev)
+    ws_ = []
+    for l in range(L):
+        w = WL.gpu_weight_f32(p.N, p.K, seed=10_000 + l * 16 + i, device=dev)
+        ws_.append(api.nf4_quantize(w, code, ncode))
+        del w
+    ins = [WL.gpu_normal_bf16(M, p.K if d == "fwd" else p.N, seed=30_000 + l, device=dev) for l in range(L)]
+    out = torch.empty((M, p.N if d == "fwd" else p.K), dtype=torch.bfloat16, device=dev)
+    ws = workspace_for(torch, api, [p], [M], dev)
+
+    def one():
+        for l in range(L):
+            if d == "fwd":
+                api.nf4_matmul_fwd(ins[l], ws_[l], out=out, ws=ws)
+            else:
+                api.nf4_matmul_bwd_input(ins[l], ws_[l], out=out, ws=ws)
+
+    ms = timed(torch, stream, one, args.steps, args.warmup) / L
+    flops = 2.0 * M * p.N * p.K
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps({"shape": args.only, "M": M, "N": p.N, "K": p.K, "ops": L * (args.steps + args.warmup),
+                      "avg_us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                      "copy_bytes": args.copy_bytes}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -263,10 +318,15 @@ def main():
               f"of x and grad_y against a replica of the frozen packed weights).", file=sys.stderr)
         sys.exit(2)
 
+    if args.only:
+        run_only(args)
+        return
+
     import torch
 
     import workloads as WL
     from nf4_bit_weight_amd import api
+    from nf4_bit_weight_amd import profiling
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -327,6 +387,12 @@ def main():
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
         "avg_launch_us": round(dom_avg_s * 1e6, 2),
     }
+    # HBM bytes per launch from the committed rocprofv3 counter summary of this
+    # shape, if it was measured on the kernel sources built here
+    fig = profiling.read_traffic(traffic_file(dom[0], p.name, M))
+    if fig is not None:
+        roofline["traffic"] = fig["bytes_per_op"]
+        roofline["traffic_source"] = os.path.relpath(traffic_file(dom[0], p.name, M), ROOT)
 
     extra = {}
     if not args.no_extra:

@@ -57,6 +57,7 @@ struct GemmParams {
   int64_t M;                // rows of A and C
   int32_t E;
   int32_t splits;
+  int32_t m_tiles;          // row tiles (grouped: an upper bound)
 };
 
 // BM x BN output tile, contraction step BK chosen so the weight tile holds
@@ -64,7 +65,7 @@ struct GemmParams {
 // 4*C consumer waves (C = 1 or 2), i.e. per SIMD one producer and C
 // consumers:
 //   producer : copies the activation tile (global -> LDS), fetches the packed
-//              weights two steps ahead and expands one (row, 64-block) unit
+//              weights kPD steps ahead and expands one (row, 64-block) unit
 //              per thread into the LDS weight tile -- pure VALU / memory work;
 //   consumer : reads MFMA fragments from LDS and issues the MFMAs of its
 //              (BM / CW_M) x (BN / CW_N) part of the tile.
@@ -72,6 +73,9 @@ struct GemmParams {
 // VALU ops cost ~54 cycles instead of 32), but the SIMD issues one wave's
 // VALU and another wave's MFMA in the same cycles, so splitting the roles
 // makes a step cost ~max(expansion, MFMA) instead of their sum.
+// Global-memory latency (several steps' worth under load) is hidden by
+// prefetch depth: the activation tile lives in an NA-stage LDS ring (copy
+// issued NA-1 steps ahead) and the packed weights in kPD register sets.
 template <int BM, int BN_, bool TRANS, int C_>
 struct Tile {
   static constexpr int BN = BN_;
@@ -88,13 +92,33 @@ struct Tile {
   static constexpr int kUnits = BK / 8;             // 16-byte units per tile row
   static constexpr int kARowsPerInstr = 64 / kUnits;
   static constexpr int kARowsPerWave = BM / 4;      // activation rows per producer wave
+  static constexpr int kAInstr = kARowsPerWave / kARowsPerInstr;
   static constexpr int kBTPitch = BN + 16;          // backward weight tile pitch (elements)
   static constexpr int kAElems = BM * BK;
   static constexpr int kBElems = TRANS ? BK * kBTPitch : BN * BK;
-  static constexpr int kLdsBytes = 2 * (kAElems + kBElems) * 2;
+  // LDS: NA activation stages, 2 expanded weight buffers and PD staging
+  // slots of packed weights (kWSlot bytes each: 256 units x 32 B, then
+  // 256 x 4 B block scales, then 256 x 4 B nested scales), within 159 KB
+  // (1 KB is the static nested table).  Deepest prefetch that fits, in the
+  // order (4, 4), (2, 4), (2, 2).
+  static constexpr int kWSlot = 10240;
+  static constexpr int kFixed = 2 * kBElems * 2;
+  static constexpr int kBudget = 159 * 1024;
+  static constexpr bool kFit44 = kFixed + 4 * kAElems * 2 + 4 * kWSlot <= kBudget;
+  static constexpr bool kFit24 = kFixed + 2 * kAElems * 2 + 4 * kWSlot <= kBudget;
+  static constexpr int NA = kFit44 ? 4 : 2;         // activation stages
+  static constexpr int kPD = (kFit44 || kFit24) ? 4 : 2;   // weight slots = prefetch distance
+  static constexpr int kAOff = 0;
+  static constexpr int kBOff = NA * kAElems * 2;
+  static constexpr int kWOff = kBOff + kFixed;
+  static constexpr int kLdsBytes = kWOff + kPD * kWSlot;
+  // Consumers double-buffer their fragments when the registers allow it
+  // (every wave of the kernel gets 512 / waves-per-SIMD registers).
+  static constexpr int kRegs = (512 / (1 + C)) & ~7;
+  static constexpr bool kFragDB = MI * NI * 16 + 2 * (MI + NI) * 4 + 32 <= kRegs;
   static_assert(MI >= 1 && NI >= 1, "tile too small");
   static_assert(kARowsPerWave % kARowsPerInstr == 0, "A copy split");
-  static_assert(kLdsBytes + 1024 <= 160 * 1024, "LDS budget of one workgroup");
+  static_assert(kLdsBytes <= kBudget, "LDS budget of one workgroup");
 };
 
 // 16-byte unit u of row r of a [rows][BK] tile is stored at unit u ^ ((r >> 1) & 7):
@@ -102,24 +126,47 @@ struct Tile {
 // measured ~1.4x the LDS throughput of u ^ (r & 7) on gfx950.
 __device__ __forceinline__ int swz(int r, int u) { return u ^ ((r >> 1) & 7); }
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2.  Linear id L is mapped to tile t so that XCD j runs the
+// contiguous tile range [j*q + min(j, r), ...) (q = T/8, r = T%8); tiles are
+// ordered (column tile, split, row tile) with the row tile fastest, so the
+// row tiles sharing one weight tile run together on one XCD and the weight
+// tile is fetched from HBM into that L2 once.
+__device__ __forceinline__ int xcd_tile(int L, int T) {
+  const int xcd = L & 7, idx = L >> 3;
+  const int q = T >> 3, r = T & 7;
+  return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 template <int BM, int BN, bool TRANS, bool NESTED, bool GROUPED, int C>
 __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
   using T = Tile<BM, BN, TRANS, C>;
   constexpr int BK = T::BK;
+  constexpr int NA = T::NA;
+  constexpr int PD = T::kPD;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ float sncode[256];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across the wave; saying so keeps M0 (the LDS
+  // destination of global_load_lds) and the role branch scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t N = p.w.N, K = p.w.K;
   const int64_t Nc = TRANS ? K : N;        // output columns
   const int64_t Kc = TRANS ? N : K;        // contraction length
   const int ktiles = static_cast<int>((Kc + BK - 1) / BK);
 
-  // ---- rows owned by this workgroup ---------------------------------------
+  // ---- tile owned by this workgroup -----------------------------------------
+  const int t = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = t % p.m_tiles;
+  const int cz = t / p.m_tiles;
+  const int z = cz % p.splits;
+  const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
   int64_t row0, row_end, wrow_base = 0;
   if constexpr (GROUPED) {
-    const int mt = blockIdx.y;
     int acc = 0, e_found = -1;
     int64_t lo = 0, hi = 0;
     for (int e = 0; e < p.E; ++e) {
@@ -135,17 +182,32 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
     row_end = hi;
     wrow_base = static_cast<int64_t>(e_found) * N;
   } else {
-    row0 = static_cast<int64_t>(blockIdx.y) * BM;
+    row0 = static_cast<int64_t>(mt) * BM;
     row_end = p.M;
   }
-  const int64_t col0 = static_cast<int64_t>(blockIdx.x) * BN;
-  const int z = blockIdx.z;
   const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
   const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
+  const int n = ke - kb;                   // steps of this workgroup
 
-  auto a_tile = [&](int buf) { return lds + buf * T::kAElems; };
-  auto b_tile = [&](int buf) { return lds + 2 * T::kAElems + buf * T::kBElems; };
+  auto a_tile = [&](int stage) { return lds + stage * T::kAElems; };
+  auto b_tile = [&](int buf) { return lds + NA * T::kAElems + buf * T::kBElems; };
+  char* const w_area = reinterpret_cast<char*>(lds) + T::kWOff;
 
+  // Step i (0 <= i < n) of the contraction uses activation stage i % NA and
+  // weight buffer i % 2.  During step i the consumers multiply step i while
+  // the producers (a) issue the activation copy of step i+NA-1 into the stage
+  // step i-1 used, (b) issue the packed-weight copy of step i+PD into the
+  // staging slot step i used, (c) expand the weights of step i+1 into the
+  // buffer step i-1 used.  One workgroup barrier ends each step.  Indices
+  // past the last step are clamped to it: the copies and expansions they
+  // cause land in buffers no later step reads.
+  //
+  // Every global load of the loop is an LDS-direct copy and the staging
+  // reads are inline assembly, so the only waits on vector memory are the
+  // explicit per-step vmcnt below (the compiler's own wait insertion falls
+  // back to vmcnt(0) once a loop mixes LDS-direct copies with loads into
+  // registers that are carried across iterations, which would drain the
+  // whole prefetch pipeline every iteration).
   if (wave < 4) {
     // =================== producer waves (threads 0..255) ======================
     float code[16];
@@ -165,56 +227,109 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
     // row and meet zero weights.
     const int a_r_in = lane / T::kUnits;
     const int a_unit = lane % T::kUnits;
-    auto issue_a = [&](int kt, int buf) {
+    auto issue_a = [&](int i, int stage) {
+      const int kt = kb + (i < n ? i : n - 1);
       const int64_t c0 = static_cast<int64_t>(kt) * BK;
 #pragma unroll
-      for (int i = 0; i < T::kARowsPerWave / T::kARowsPerInstr; ++i) {
-        const int r = wave * T::kARowsPerWave + i * T::kARowsPerInstr + a_r_in;
+      for (int j = 0; j < T::kAInstr; ++j) {
+        const int r = wave * T::kARowsPerWave + j * T::kARowsPerInstr + a_r_in;
         int64_t row = row0 + r;
         row = row < row_end ? row : row_end - 1;
         int64_t col = c0 + 8 * swz(r, a_unit);
         col = col < Kc ? col : Kc - 8;
         const uint16_t* src = p.A + row * Kc + col;
-        uint16_t* dst = a_tile(buf) + (wave * T::kARowsPerWave + i * T::kARowsPerInstr) * BK;
+        uint16_t* dst = a_tile(stage) + (wave * T::kARowsPerWave + j * T::kARowsPerInstr) * BK;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
       }
     };
 
-    // Weight tile units, fetched two steps ahead into registers:
-    //   forward : thread t expands W row (col0 + t % BN), block (kt*BK/64 + t / BN)
-    //   backward: thread t expands W row (kt*BK + t % BK), block (col0/64 + t / BK)
-    // Out-of-range rows or columns load a valid address and are then replaced
-    // by all-7 nibbles (code 0) with scale 0, so the expansion writes zeros
-    // without a branch.
-    struct BRaw {
-      u32x4_t pk[2];
-      uint32_t sraw;    // u8 nested index or fp32 bits of the plain absmax
-      float s2;
-      bool valid;
+    // Weight units.  Unit u of a step covers
+    //   forward : W row (col0 + u % BN), block (kt*BK/64 + u / BN)
+    //   backward: W row (kt*BK + u % BK), block (col0/64 + u / BK)
+    // and its element offset is off0 + kt * dstep.  Producer thread t expands
+    // unit t; the copy of unit u's 32 packed bytes is done by lanes 2u, 2u+1
+    // (mod 64) of the same wave, the copy of its scale by lane u of the same
+    // wave, so each wave reads only what its own copies wrote.  Units past
+    // the matrix copy unit 0 of the tensor and are replaced by zero weights.
+    struct Unit {
+      int64_t off0;
+      int var_in;
+      bool fixed_ok;
     };
-    auto load_b = [&](int kt, BRaw& r) {
-      const int64_t c0 = static_cast<int64_t>(kt) * BK;
-      int64_t wrow, wcol;
+    const int64_t dstep = TRANS ? static_cast<int64_t>(BK) * K : BK;
+    const int64_t var_lim = TRANS ? N : K;
+    auto unit_of = [&](int u) {
+      Unit g;
       if constexpr (TRANS) {
-        wrow = c0 + (tid % BK);
-        wcol = col0 + 64 * (tid / BK);
+        const int64_t wcol = col0 + 64 * (u / BK);
+        g.fixed_ok = wcol < K;
+        g.off0 = (wrow_base + u % BK) * K + wcol;
+        g.var_in = u % BK;
       } else {
-        wrow = col0 + (tid % BN);
-        wcol = c0 + 64 * (tid / BN);
+        const int64_t wrow = col0 + (u % BN);
+        g.fixed_ok = wrow < N;
+        g.off0 = (wrow_base + wrow) * K + 64 * (u / BN);
+        g.var_in = 64 * (u / BN);
       }
-      r.valid = (wrow < N) && (wcol < K);
-      const int64_t flat = r.valid ? (wrow_base + wrow) * K + wcol : 0;   // multiple of 64
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + flat / 2);
-      r.pk[0] = src[0];
-      r.pk[1] = src[1];
-      const int64_t b = flat / kBlock;
+      return g;
+    };
+    auto unit_valid = [&](const Unit& g, int kt) {
+      return g.fixed_ok & (static_cast<int64_t>(kt) * BK + g.var_in < var_lim);
+    };
+    auto unit_flat = [&](const Unit& g, int kt) -> uint64_t {
+      return unit_valid(g, kt) ? static_cast<uint64_t>(g.off0 + kt * dstep) : 0;   // multiple of 64
+    };
+    const Unit own = unit_of(tid);
+    const Unit cp0 = unit_of(64 * wave + (lane >> 1));
+    const Unit cp1 = unit_of(64 * wave + 32 + (lane >> 1));
+    auto issue_w = [&](int i, int slot) {
+      const int kt = kb + (i < n ? i : n - 1);
+      char* sl = w_area + slot * T::kWSlot;
+      const uint8_t* s0 = p.w.packed + (unit_flat(cp0, kt) >> 1) + 16 * (lane & 1);
+      const uint8_t* s1 = p.w.packed + (unit_flat(cp1, kt) >> 1) + 16 * (lane & 1);
+      __builtin_amdgcn_global_load_lds(s0, (lds_void_t*)(sl + 2048 * wave), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(s1, (lds_void_t*)(sl + 2048 * wave + 1024), 16, 0, 0);
+      const uint64_t b = unit_flat(own, kt) >> 6;
       if constexpr (NESTED) {
-        r.sraw = static_cast<const uint8_t*>(p.w.absmax)[b];
-        r.s2 = p.w.nested_absmax[b / kNestedBlock];
+        // one byte per lane, written zero-extended to the lane's dword
+        __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.w.absmax) + b,
+                                         (lds_void_t*)(sl + 8192 + 256 * wave), 1, 0, 0);
+        __builtin_amdgcn_global_load_lds(p.w.nested_absmax + (b >> 8),
+                                         (lds_void_t*)(sl + 9216 + 256 * wave), 4, 0, 0);
       } else {
-        r.sraw = __float_as_uint(static_cast<const float*>(p.w.absmax)[b]);
+        __builtin_amdgcn_global_load_lds(static_cast<const float*>(p.w.absmax) + b,
+                                         (lds_void_t*)(sl + 8192 + 256 * wave), 4, 0, 0);
       }
     };
+    // LDS byte addresses of this thread's staged unit and scale in slot 0
+    const uint32_t st_unit = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) + 32 * tid;
+    const uint32_t st_scale = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) + 8192 + 4 * tid;
+    const uint32_t st_ncode = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)sncode));
+    struct Staged {
+      u32x4_t pk0, pk1;
+      uint32_t sc, s2;
+    };
+#define NF4_READ_UNIT(OFF)                                                                 \
+  asm volatile("ds_read_b128 %0, %4 offset:" #OFF "\n\t"                                   \
+               "ds_read_b128 %1, %4 offset:" #OFF "+16\n\t"                                \
+               "ds_read_b32 %2, %5 offset:" #OFF "\n\t"                                    \
+               "ds_read_b32 %3, %5 offset:" #OFF "+1024\n\t"                               \
+               "s_waitcnt lgkmcnt(0)"                                                      \
+               : "=v"(r.pk0), "=v"(r.pk1), "=v"(r.sc), "=v"(r.s2)                          \
+               : "v"(st_unit), "v"(st_scale)                                               \
+               : "memory")
+    auto read_unit = [&](int slot) {
+      Staged r;
+      static_assert(T::kWSlot == 10240, "slot offsets below");
+      switch (slot) {
+        case 0: NF4_READ_UNIT(0); break;
+        case 1: NF4_READ_UNIT(10240); break;
+        case 2: NF4_READ_UNIT(20480); break;
+        default: NF4_READ_UNIT(30720); break;
+      }
+      return r;
+    };
+#undef NF4_READ_UNIT
     auto b_dst = [&](int buf, int d) -> uint16_t* {
       if constexpr (TRANS) {
         return b_tile(buf) + (tid % BK) * T::kBTPitch + 64 * (tid / BK) + 8 * d;
@@ -223,64 +338,86 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
         return b_tile(buf) + row * BK + 8 * swz(row, 8 * (tid / BN) + d);
       }
     };
-    auto expand_into = [&](const BRaw& r, int buf) {
+    // expand the staged unit of step i (slot `slot`) into weight buffer `buf`
+    auto expand_into = [&](int i, int slot, int buf) {
+      const int kt = kb + (i < n ? i : n - 1);
+      const bool valid = unit_valid(own, kt);
+      const Staged r = read_unit(slot);
       float a;
-      if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[r.sraw], r.s2), off);
-      else a = __uint_as_float(r.sraw);
+      if constexpr (NESTED) {
+        float nc;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(nc) : "v"(st_ncode + 4 * (r.sc & 0xFF)) : "memory");
+        a = __fadd_rn(__fmul_rn(nc, __uint_as_float(r.s2)), off);
+      } else {
+        a = __uint_as_float(r.sc);
+      }
       const u32x4_t zero_codes = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      const u32x4_t pk0 = r.valid ? r.pk[0] : zero_codes;
-      const u32x4_t pk1 = r.valid ? r.pk[1] : zero_codes;
-      const Lut t = make_lut(code, r.valid ? a : 0.f);
+      const u32x4_t pk0 = valid ? r.pk0 : zero_codes;
+      const u32x4_t pk1 = valid ? r.pk1 : zero_codes;
+      const Lut lt = make_lut(code, valid ? a : 0.f);
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         uint32_t o[4];
-        expand8(d < 4 ? pk0[d] : pk1[d - 4], t, o);
+        expand8(d < 4 ? pk0[d] : pk1[d - 4], lt, o);
         *reinterpret_cast<u32x4_t*>(b_dst(buf, d)) = u32x4_t{o[0], o[1], o[2], o[3]};
       }
     };
-    // End of a step: the activation copy issued this step has landed
-    // (vector-memory operations complete in issue order, so vmcnt(kWLoads)
-    // leaves only the weight loads in flight) and the expansion's LDS writes
-    // are done; then the workgroup barrier.
-    constexpr int kWLoads = NESTED ? 4 : 3;          // dwordx4 x2 + scale load(s)
+    // Vector-memory operations complete in issue order; step i issues the
+    // activation copy of step i+NA-1 (kA operations), then the weight copy
+    // of step i+PD (kW).  At the end of step i the activation copy of step
+    // i+1 (multiplied in step i+1) and the weight copy of step i+2 (expanded
+    // in step i+1) must have landed, i.e. at most kWait later operations may
+    // still be in flight.
+    constexpr int kA = T::kAInstr;
+    constexpr int kW = NESTED ? 4 : 3;
+    constexpr int kAfterA = kW + (NA - 2) * (kA + kW);
+    constexpr int kAfterW = (PD - 2) * (kA + kW);
+    constexpr int kWait = kAfterA < kAfterW ? kAfterA : kAfterW;
+    static_assert(kWait < 64, "vmcnt range");
+    auto wait_vm = [](auto cnt) {
+      constexpr int c = decltype(cnt)::value;
+      // vmcnt(c) lgkmcnt(0); vmcnt is split over bits 3:0 and 15:14
+      __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | (7 << 4));
+    };
     auto end_step = [&]() {
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt((kWLoads & 15) | (7 << 4));   // vmcnt(kWLoads) lgkmcnt(0)
+      wait_vm(ic<kWait>{});
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (kb < ke) {
+    if (n > 0) {
       if constexpr (NESTED) __syncthreads();      // sncode filled (matched by consumers)
-      BRaw r0, r1;
-      issue_a(kb, 0);
-      load_b(kb, r0);
-      load_b(kb + 1 < ke ? kb + 1 : kb, r1);
-      expand_into(r0, 0);
-      __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+      for (int j = 0; j < NA - 1; ++j) issue_a(j, j);
+#pragma unroll
+      for (int j = 0; j < PD; ++j) issue_w(j, j);
+      wait_vm(ic<(PD - 1) * kW>{});                // every activation copy, weights of step 0
+      expand_into(0, 0, 0);
+      wait_vm(ic<(PD - 2) * kW>{});                // weights of step 1
       __syncthreads();
-      // invariant at the top: buffer 0 holds step s, r1 holds step s+1
-      int s = kb;
-      for (; s + 2 < ke; s += 2) {
-        issue_a(s + 1, 1);
+      auto step = [&](int i, auto ph) {
+        constexpr int P = decltype(ph)::value;
+        issue_a(i + NA - 1, (P + NA - 1) % NA);
+        issue_w(i + PD, P % PD);
         __builtin_amdgcn_sched_barrier(0);
-        load_b(s + 2, r0);
-        expand_into(r1, 1);
+        expand_into(i + 1, (P + 1) % PD, (P + 1) % 2);
         end_step();
-        issue_a(s + 2, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(s + 3 < ke ? s + 3 : s + 2, r1);
-        expand_into(r0, 0);
-        end_step();
+      };
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {
+        step(i, ic<0>{});
+        step(i + 1, ic<1>{});
+        step(i + 2, ic<2>{});
+        step(i + 3, ic<3>{});
       }
-      if (s + 1 < ke) {
-        issue_a(s + 1, 1);
-        expand_into(r1, 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
+      if (i < n) step(i, ic<0>{});
+      if (i + 1 < n) step(i + 1, ic<1>{});
+      if (i + 2 < n) step(i + 2, ic<2>{});
+      __builtin_amdgcn_s_waitcnt(0);               // no copy into LDS outlives the workgroup
     }
     return;
   }
@@ -297,56 +434,89 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // fragment addresses (elements) that do not depend on the step
-  int a_row[T::MI];
+  // Fragment addresses.  Fragment i of k-step kk reads A row
+  // wm*WM + 32i + r32, 16-byte unit 2kk + h, stored at unit
+  // (2kk + h) ^ ((row >> 1) & 7) = 2kk ^ y with y = h ^ ((r32 >> 1) & 7)
+  // (WM and WN are multiples of 32, and 2kk and h use disjoint bits).  So a
+  // lane needs one address per (kk mod 4) for A and one for B; stage, buffer,
+  // fragment index and kk >= 4 (unit + 8) are compile-time offsets that fit
+  // the instruction's immediate field.
+  const int y = h ^ ((r32 >> 1) & 7);
+  const char* pa[4];
+  const char* pb[4];
+  {
+    const char* a0 = reinterpret_cast<const char*>(lds) + (wm * T::WM + r32) * BK * 2;
+    const char* b0 = reinterpret_cast<const char*>(lds + NA * T::kAElems);
 #pragma unroll
-  for (int i = 0; i < T::MI; ++i) a_row[i] = wm * T::WM + 32 * i + r32;
-  // backward transposing read: lane l of 16-lane group g, index s = l%16
-  const int tg = lane >> 4, ts = lane & 15;
-  const int tr_row = 8 * (tg >> 1) + (ts >> 2);                     // + 16*kk + 4*half
-  const int tr_col = wn * T::WN + 16 * (tg & 1) + 4 * (ts & 3);     // + 32*j
+    for (int q = 0; q < 4; ++q) {
+      pa[q] = a0 + 16 * ((2 * q) ^ y);
+      if constexpr (TRANS) {
+        // backward transposing read: lane l of 16-lane group g, index s = l%16
+        const int tg = lane >> 4, ts = lane & 15;
+        const int tr_row = 8 * (tg >> 1) + (ts >> 2);                 // + 16*kk + 4*half
+        const int tr_col = wn * T::WN + 16 * (tg & 1) + 4 * (ts & 3); // + 32*j
+        pb[q] = b0 + (tr_row * T::kBTPitch + tr_col) * 2;
+      } else {
+        pb[q] = b0 + (wn * T::WN + r32) * BK * 2 + 16 * ((2 * q) ^ y);
+      }
+    }
+  }
 
   struct Frags {
     bf16x8_t a[T::MI];
     bf16x8_t b[T::NI];
   };
-  auto load_frags = [&](int buf, int kk, Frags& f) {
-    const uint16_t* a_s = a_tile(buf);
+  // stage, buf and kk are compile-time constants at every call
+  auto load_frags = [&](int stage, int buf, int kk, Frags& f) {
 #pragma unroll
     for (int i = 0; i < T::MI; ++i)
-      f.a[i] = *reinterpret_cast<const bf16x8_t*>(a_s + a_row[i] * BK + 8 * swz(a_row[i], 2 * kk + h));
-    const uint16_t* b_s = b_tile(buf);
+      f.a[i] = *reinterpret_cast<const bf16x8_t*>(pa[kk & 3] + stage * T::kAElems * 2 +
+                                                  (kk >> 2) * 128 + i * 32 * BK * 2);
 #pragma unroll
     for (int j = 0; j < T::NI; ++j) {
       if constexpr (TRANS) {
-        const uint16_t* src = b_s + (16 * kk + tr_row) * T::kBTPitch + tr_col + 32 * j;
+        const char* src = pb[0] + buf * T::kBElems * 2 + (16 * kk * T::kBTPitch + 32 * j) * 2;
         s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * T::kBTPitch));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * T::kBTPitch * 2));
         u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
         f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
       } else {
-        const int brow = wn * T::WN + 32 * j + r32;
-        f.b[j] = *reinterpret_cast<const bf16x8_t*>(b_s + brow * BK + 8 * swz(brow, 2 * kk + h));
+        f.b[j] = *reinterpret_cast<const bf16x8_t*>(pb[kk & 3] + buf * T::kBElems * 2 +
+                                                    (kk >> 2) * 128 + j * 32 * BK * 2);
       }
     }
   };
-  // Fragments of k-step kk+1 are read while the MFMAs of kk run; the
-  // scheduling fence per k-step keeps the compiler from hoisting every
-  // step's reads ahead (two fragment sets live at most).
-  auto compute = [&](int buf) {
-    Frags f0, f1;
-    load_frags(buf, 0, f0);
+  auto mfmas = [&](const Frags& f) {
 #pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      Frags& fc = (kk & 1) ? f1 : f0;
-      Frags& fn = (kk & 1) ? f0 : f1;
-      if (kk + 1 < T::KK) load_frags(buf, kk + 1, fn);
+    for (int i = 0; i < T::MI; ++i)
 #pragma unroll
-      for (int i = 0; i < T::MI; ++i)
+      for (int j = 0; j < T::NI; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  // With double-buffered fragments the reads of k-step kk+1 are issued
+  // while the MFMAs of kk run (a scheduling fence per k-step keeps at most
+  // two sets live); otherwise the other consumer wave of the SIMD covers
+  // the read latency.
+  auto compute = [&](int stage, int buf) {
+    if constexpr (T::kFragDB) {
+      Frags f0, f1;
+      load_frags(stage, buf, 0, f0);
 #pragma unroll
-        for (int j = 0; j < T::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int kk = 0; kk < T::KK; ++kk) {
+        Frags& fc = (kk & 1) ? f1 : f0;
+        Frags& fn = (kk & 1) ? f0 : f1;
+        if (kk + 1 < T::KK) load_frags(stage, buf, kk + 1, fn);
+        mfmas(fc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        Frags f;
+        load_frags(stage, buf, kk, f);
+        mfmas(f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   auto end_step = [&]() {
@@ -358,23 +528,24 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  if (kb < ke) {
+  if (n > 0) {
     if constexpr (NESTED) __syncthreads();        // matches the producers' sncode barrier
-    __syncthreads();                              // step kb is in buffer 0
-    int s = kb;
-    for (; s + 2 < ke; s += 2) {
-      compute(0);
+    __syncthreads();                              // step 0 is in stage 0 / buffer 0
+    auto step = [&](auto ph) {
+      constexpr int P = decltype(ph)::value;
+      compute(P % NA, P % 2);
       end_step();
-      compute(1);
-      end_step();
+    };
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      step(ic<0>{});
+      step(ic<1>{});
+      step(ic<2>{});
+      step(ic<3>{});
     }
-    if (s + 1 < ke) {
-      compute(0);
-      __syncthreads();
-      compute(1);
-    } else {
-      compute(0);
-    }
+    if (i < n) step(ic<0>{});
+    if (i + 1 < n) step(ic<1>{});
+    if (i + 2 < n) step(ic<2>{});
   }
 
   // ---- epilogue ----------------------------------------------------------------
@@ -437,9 +608,11 @@ hipError_t launch_tiled(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hi
     return true;
   }();
   (void)attr_done;
-  dim3 grid(static_cast<unsigned>((n_cols + BN - 1) / BN), static_cast<unsigned>(m_tiles),
-            static_cast<unsigned>(p.splits));
-  kern<<<grid, T::kThreads, T::kLdsBytes, stream>>>(p);
+  GemmParams q = p;
+  q.m_tiles = static_cast<int32_t>(m_tiles);
+  const int64_t tiles = ((n_cols + BN - 1) / BN) * m_tiles * p.splits;
+  if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kern<<<dim3(static_cast<unsigned>(tiles)), T::kThreads, T::kLdsBytes, stream>>>(q);
   return hipGetLastError();
 }
 
@@ -488,8 +661,18 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t nc = (kind == GemmKind::kFwd) ? N : K;
   const int64_t kc = (kind == GemmKind::kFwd) ? K : N;
   pl.small_m = false;
-  pl.bm = (M <= 64) ? 64 : (M <= 128 ? 128 : 256);
-  pl.bn = 256;
+  // Tile choice by the size of the product (measured on MI355X over the
+  // Llama-3.1-8B projections at M = 512 and the Qwen2.5-32B ones at
+  // M = 2048): large products take 256 x 256 (each expanded weight serves 256
+  // rows), mid-size ones 128 x 128 (4x the tiles), small ones 64 x 128.
+  const double macs = static_cast<double>(M) * static_cast<double>(nc) * static_cast<double>(kc);
+  if (macs >= 2e10 && M > 128) {
+    pl.bm = 256; pl.bn = 256;
+  } else if (macs >= 4e9 && M > 64) {
+    pl.bm = 128; pl.bn = 128;
+  } else {
+    pl.bm = 64; pl.bn = 128;
+  }
   // Tuning overrides (documented): NF4_BM, NF4_BN, NF4_CONSUMERS, NF4_SPLITS.
   const int o_bm = env_int("NF4_BM"), o_bn = env_int("NF4_BN"), o_s = env_int("NF4_SPLITS");
   const int o_c = env_int("NF4_CONSUMERS");

@@ -1,0 +1,165 @@
+"""Summaries of rocprofv3 output for the fused NF4 kernels.
+
+Turns the CSV files rocprofv3 writes (``--kernel-trace --stats`` and
+``--pmc``) into the short text summaries kept with the project, and reads the
+HBM-traffic figure back for the benchmark line.  Needs no GPU.
+
+    python -m nf4_bit_weight_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
+    python -m nf4_bit_weight_amd.profiling traffic <fetch_counter_collection.csv>
+           <write_counter_collection.csv> <copy_bytes> <ops> <out.md> "<shape>" "<command>"
+
+Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 run
+each) summed over the dispatches of the measured operation (the fused GEMM
+and, when the contraction is split, its reduction), divided by the number of
+operations, each scaled by the factor that maps the same counter onto the
+known byte count of a plain device-to-device copy measured in the same run.
+"""
+
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/nf4_gemm.hip", "csrc/nf4_device.hpp")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+FUSED_KERNELS = ("k_gemm<", "k_splitk_reduce")
+
+
+def kernel_source_sha256() -> str:
+    """Hash of the sources the fused GEMM is built from: a traffic figure
+    taken from counters is valid only for the kernel it was measured on."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _short(name: str, width: int = 96) -> str:
+    name = name.replace("nf4::(anonymous namespace)::", "").replace("(GemmParams)", "")
+    name = re.sub(r"^void ", "", name)
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def summarize_stats(stats_csv: str, out_md: str, command: str, top: int = 12) -> None:
+    rows = list(csv.DictReader(open(stats_csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [
+        "# rocprofv3 kernel statistics",
+        "",
+        "Command (run from the repository root on one MI355X):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | calls | total ms | avg us | min us | max us | % |",
+        "|---|---:|---:|---:|---:|---:|---:|",
+    ]
+    for r in rows[:top]:
+        lines.append(
+            f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+            f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+            f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(pmc_csv: str, counter: str):
+    """{dispatch_id: (kernel_name, value)} for one counter."""
+    out = {}
+    for r in csv.DictReader(open(pmc_csv)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, val = r["Kernel_Name"], float(r["Counter_Value"])
+        if d in out:
+            out[d] = (name, out[d][1] + val)
+        else:
+            out[d] = (name, val)
+    return out
+
+
+def traffic_figures(fetch_csv: str, write_csv: str, copy_bytes: int, ops: int) -> dict:
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = _per_dispatch(path, counter)
+        copies = [v for (n, v) in disp.values() if COPY_KERNEL in n]
+        fused = [v for (n, v) in disp.values() if any(k in n for k in FUSED_KERNELS)]
+        if not copies or not fused:
+            raise RuntimeError(f"{path}: no copy or no fused-kernel dispatches for {counter}")
+        copy_kib = max(copies)                     # the calibration copy is the largest one
+        factor = (copy_bytes / 1024.0) / copy_kib
+        res[counter] = {
+            "copy_kib": round(copy_kib, 1), "factor": round(factor, 4),
+            "fused_dispatches": len(fused),
+            "kib_per_op_raw": round(sum(fused) / ops, 1),
+            "bytes_per_op": round(sum(fused) / ops * 1024.0 * factor),
+        }
+    res["bytes_per_op"] = res["FETCH_SIZE"]["bytes_per_op"] + res["WRITE_SIZE"]["bytes_per_op"]
+    return res
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_bytes, ops, out_md, shape, command) -> dict:
+    fig = traffic_figures(fetch_csv, write_csv, int(copy_bytes), int(ops))
+    fig["shape"] = shape
+    fig["ops"] = int(ops)
+    fig["copy_bytes"] = int(copy_bytes)
+    fig["kernel_source_sha256"] = kernel_source_sha256()
+    lines = [
+        f"# HBM traffic of the fused NF4 GEMM: {shape}",
+        "",
+        "Two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"Each counter is scaled by the factor that maps it onto a plain {copy_bytes} B "
+        f"device-to-device copy (`{COPY_KERNEL}`) measured in the same run; the sum over the "
+        f"fused GEMM and split-K reduction dispatches is divided by the {ops} operations.",
+        "",
+        "```json",
+        json.dumps(fig, indent=1),
+        "```",
+    ]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return fig
+
+
+def read_traffic(md_path: str):
+    """The figures of a traffic summary, or None when the file is missing or
+    was measured on other kernel sources."""
+    try:
+        text = open(md_path).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    fig = json.loads(m.group(1))
+    if fig.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return fig
+
+
+def main(argv):
+    if len(argv) >= 4 and argv[0] == "stats":
+        summarize_stats(argv[1], argv[2], argv[3])
+    elif len(argv) >= 8 and argv[0] == "traffic":
+        fig = summarize_traffic(argv[1], argv[2], int(argv[3]), int(argv[4]), argv[5], argv[6], argv[7])
+        print(json.dumps(fig))
+    else:
+        print(__doc__)
+        return 2
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
