@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--only", default=None, metavar="DIR_PROJ",
                     help="time one shape of the step (e.g. fwd_gate: the 32 layers' forward gate "
                          "projections) and nothing else; used for profiling")
+    ap.add_argument("--m", type=int, default=0,
+                    help="with --only: rows of x (default: the step's M = 512)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only: then run one plain device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -151,10 +153,29 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
                 for i in range(len(projs)):
                     api.nf4_matmul_fwd(xs[i], llama_weights[l][i], out=ys[i], ws=ws)
 
-        ms = timed(torch, stream, one_pass, steps=5, warmup=2)
+        # 224 back-to-back launches of a few microseconds each: issuing them
+        # from Python costs more than running them, so the pass is captured
+        # once into a HIP graph and replayed; the replay's outputs must equal
+        # the eager pass bit for bit.
+        one_pass()
+        torch.cuda.synchronize()
+        eager = [y.clone() for y in ys]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_pass()
+        for y in ys:
+            y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(eager, ys))
+        ms = timed(torch, stream, graph.replay, steps=10, warmup=3)
+        ms_eager = timed(torch, stream, one_pass, steps=3, warmup=1)
         gbs = wbytes / (ms * 1e-3) / 1e9
         dec[f"M={M}"] = {"us_per_pass": round(ms * 1e3, 1), "weight_GBps": round(gbs, 1),
-                         "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4)}
+                         "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4),
+                         "graph_replay_bitwise_equal": same,
+                         "us_per_pass_eager_launches": round(ms_eager * 1e3, 1)}
+        del graph
         del xs, ys, ws
     extra["decode_llama8b_fwd"] = dec
 
@@ -277,7 +298,7 @@ def run_only(args):
     projs = WL.LLAMA_8B
     i = [p.name for p in projs].index(name)
     p = projs[i]
-    M, L = WL.LLAMA_M, WL.LLAMA_LAYERS
+    M, L = (args.m or WL.LLAMA_M), WL.LLAMA_LAYERS
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     code = torch.from_numpy(WL.nf4_code_np()).to(dev)

@@ -660,7 +660,14 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   GemmPlan pl{};
   const int64_t nc = (kind == GemmKind::kFwd) ? N : K;
   const int64_t kc = (kind == GemmKind::kFwd) ? K : N;
+  // Forward at M <= 32 streams the weights (nf4_gemv.hip) unless NF4_SMALL_M=0.
+  const char* sm = getenv("NF4_SMALL_M");
+  if (kind == GemmKind::kFwd && M <= 32 && !(sm && sm[0] == '0')) {
+    plan_small_m(pl, M, N, K, cus);
+    return pl;
+  }
   pl.small_m = false;
+  pl.kc = 0;
   // Tile choice by the size of the product (measured on MI355X over the
   // Llama-3.1-8B projections at M = 512 and the Qwen2.5-32B ones at
   // M = 2048): large products take 256 x 256 (each expanded weight serves 256
@@ -673,7 +680,8 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   } else {
     pl.bm = 64; pl.bn = 128;
   }
-  // Tuning overrides (documented): NF4_BM, NF4_BN, NF4_CONSUMERS, NF4_SPLITS.
+  // Tuning overrides (documented): NF4_BM, NF4_BN, NF4_CONSUMERS, NF4_SPLITS
+  // (tiled kernel); NF4_SMALL_M=0 sends M <= 32 forwards to the tiled kernel.
   const int o_bm = env_int("NF4_BM"), o_bn = env_int("NF4_BN"), o_s = env_int("NF4_SPLITS");
   const int o_c = env_int("NF4_CONSUMERS");
   if (o_bm == 64 || o_bm == 128 || o_bm == 256) pl.bm = o_bm;
@@ -711,6 +719,21 @@ hipError_t launch_gemm(GemmKind kind, const GemmPlan& plan, const void* A, int64
                        const WArgs& w, void* C, void* ws, hipStream_t stream) {
   const bool trans = kind == GemmKind::kBwdInput;
   const int64_t nc = trans ? w.K : w.N;
+  if (plan.small_m) {
+    hipError_t e = launch_gemv(plan, A, M, w, C, ws, stream);
+    if (e != hipSuccess) return e;
+    count_path(3);
+    if (plan.splits > 1) {
+      const int64_t n = M * nc;
+      const int64_t threads = (n + 3) / 4;
+      k_splitk_reduce<<<static_cast<unsigned>((threads + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+          static_cast<const float*>(ws), plan.splits, n, static_cast<uint16_t*>(C));
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      count_path(5);
+    }
+    return hipSuccess;
+  }
   GemmParams p{};
   p.A = static_cast<const uint16_t*>(A);
   p.C = static_cast<uint16_t*>(C);

@@ -39,12 +39,18 @@ struct GemmPlan {
   int bn;          // output columns per tile (256 or 128)
   int consumers;   // MFMA waves per SIMD (1 or 2) beside one expanding wave
   int splits;      // contraction split count (1 = none)
-  bool small_m;    // weight-streaming forward
+  bool small_m;    // weight-streaming forward (bm = MFMA rows 16 / 32)
+  int kc;          // weight-streaming forward: contraction per split
   size_t ws_bytes; // fp32 partials when splits > 1
 };
 int device_cu_count();
 GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int32_t E);
+
+// small-M forward (nf4_gemv.hip)
+void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus);
+hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WArgs& w, void* y,
+                       void* ws, hipStream_t stream);
 
 hipError_t launch_gemm(GemmKind kind, const GemmPlan& plan, const void* A, int64_t M,
                        const WArgs& w, void* C, void* ws, hipStream_t stream);

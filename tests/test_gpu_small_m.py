@@ -1,0 +1,120 @@
+"""GPU parity of the weight-streaming forward (M <= 32) against the oracle.
+
+* the path counters show the streaming kernel ran (and the split reduction
+  when the contraction is chunked);
+* permutation probes: rows of x are unit vectors, so y[m] = W_hat[:, p(m)]
+  bit for bit -- the expansion order and the permuted staging of x agree;
+* seeded tolerance checks at M = 1 .. 32 over ragged N, contraction lengths
+  that end inside a step, plain and nested statistics;
+* full-size Llama-3.1-8B decode shapes (M = 1, 8, 32) in the launch
+  configuration the benchmark times, checked on sampled output columns;
+* bitwise run-to-run determinism, and agreement with the tiled kernel
+  (NF4_SMALL_M=0) through the same oracle.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from nf4_bit_weight_amd import api
+from oracle import nf4_oracle as O
+
+from gpu_util import DEV, abs_bits, assert_close, bits_of, ref_bits, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(M, N, K, nested, seed):
+    w = WL.weight_f32(N, K, WL.W_DECODE, 2000 + seed)
+    ref = O.quantize_nf4(w, nested=nested)
+    wq = upload(ref, N, K, nested)
+    wb = ref_bits(ref, (N, K))
+    x = WL.x_bf16(M, K, WL.W_DECODE, 2000 + seed)
+    return wq, wb, x
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+@pytest.mark.parametrize("nested", [False, True])
+def test_permutation_probe_small_m(M, nested):
+    N, K = 200, 576                      # ragged N; K ends inside a 256 step
+    w = WL.weight_f32(N, K, WL.W_DECODE, 40 + M)
+    ref = O.quantize_nf4(w, nested=nested)
+    wq = upload(ref, N, K, nested)
+    wb = ref_bits(ref, (N, K))
+    p = np.random.default_rng(M).integers(0, K, size=M)
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    x[np.arange(M), p] = 1.0
+    api.nf4_reset_path_counts()
+    y = api.nf4_matmul_fwd(x.to(DEV), wq)
+    torch.cuda.synchronize()
+    assert api.nf4_path_counts()["fwd_small_m"] == 1
+    assert np.array_equal(bits_of(y), wb.T[p])
+
+
+SMALL = [
+    (1, 64, 64), (1, 1000, 4160), (2, 136, 320), (7, 520, 1088), (16, 257, 2048),
+    (17, 96, 448), (24, 1024, 1024), (32, 130, 4096), (32, 2048, 192),
+]
+
+
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_m_vs_oracle(M, N, K, nested):
+    wq, wb, x = _setup(M, N, K, nested, M + N + K)
+    xb = WL.bf16_bits(x)
+    api.nf4_reset_path_counts()
+    y = api.nf4_matmul_fwd(x.to(DEV), wq)
+    torch.cuda.synchronize()
+    c = api.nf4_path_counts()
+    assert c["fwd_small_m"] == 1 and c["fwd_tiled"] == 0
+    splits_expected = api.nf4_workspace_bytes(1, M, N, K) > 0
+    assert (c["splitk_reduce"] == 1) == splits_expected
+    assert_close(y, O.matmul_fwd(xb, wb), f"y {M}x{N}x{K}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+
+
+def test_small_m_matches_tiled_and_repeats():
+    M, N, K = 8, 1536, 3072
+    wq, wb, x = _setup(M, N, K, True, 5)
+    xd = x.to(DEV)
+    y0 = api.nf4_matmul_fwd(xd, wq).clone()
+    for _ in range(3):
+        assert torch.equal(api.nf4_matmul_fwd(xd, wq).view(torch.int16), y0.view(torch.int16))
+    old = os.environ.get("NF4_SMALL_M")
+    os.environ["NF4_SMALL_M"] = "0"
+    try:
+        api.nf4_reset_path_counts()
+        yt = api.nf4_matmul_fwd(xd, wq)
+        torch.cuda.synchronize()
+        assert api.nf4_path_counts()["fwd_tiled"] == 1
+    finally:
+        if old is None:
+            del os.environ["NF4_SMALL_M"]
+        else:
+            os.environ["NF4_SMALL_M"] = old
+    want = O.matmul_fwd(WL.bf16_bits(x), wb)
+    assert_close(y0, want, "streaming")
+    assert_close(yt, want, "tiled")
+
+
+@pytest.mark.parametrize("M", list(WL.DECODE_MS))
+@pytest.mark.parametrize("idx", [1, 4, 6])       # k (N = 1024), gate (14336), down (K = 14336)
+def test_llama_decode_shapes(M, idx):
+    p = WL.LLAMA_8B[idx]
+    w = WL.weight_f32(p.N, p.K, WL.W_LLAMA, 0, idx)
+    ref = O.quantize_nf4(w, nested=True)
+    del w
+    wq = upload(ref, p.N, p.K, True)
+    x = WL.x_bf16(M, p.K, WL.W_LLAMA, 0)
+    xb = WL.bf16_bits(x)
+    y = api.nf4_matmul_fwd(x.to(DEV), wq)
+    # sampled output columns: the oracle dequantises only those rows of W
+    cols = np.sort(np.random.default_rng(idx * 100 + M).choice(p.N, size=96, replace=False))
+    cols[0], cols[-1] = 0, p.N - 1
+    wb = ref_bits(ref, (p.N, p.K))[cols]
+    assert_close(y[:, torch.from_numpy(cols).to(DEV)], O.matmul_fwd(xb, wb), f"{p.name} M={M}",
+                 O.matmul_fwd(abs_bits(xb), abs_bits(wb)), p.K)
+    y2 = api.nf4_matmul_fwd(x.to(DEV), wq)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not bitwise repeatable"
