@@ -570,6 +570,375 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 "ping-pong" kernel.  Eight identical waves, two per SIMD, no
+// dedicated roles.  Wave w owns the 128 x 64 output block (w / 4, w % 4)
+// with double-buffered MFMA fragments (at two waves per SIMD every wave has
+// 256 VGPRs, room the three-waves-per-SIMD producer/consumer layout lacks),
+// and every thread also expands half a weight unit (32 weights) per step.
+// The two waves sharing a SIMD (w and w + 4) run the step's two halves in
+// opposite order -- waves 0-3 multiply, then expand; waves 4-7 expand, then
+// multiply -- so the expansion VALU of one runs under the MFMAs of the other
+// (measured: another wave's VALU leaves MFMA throughput intact).
+// Staging as in k_gemm: LDS-direct copies of the activation tile (2 stages)
+// and of the packed weights and scales (2 slots), one explicit vmcnt per
+// step, one barrier per step.  A wave's six copy instructions of a step are
+// spread over the first half of its step (between MFMA groups or between
+// expansion groups) rather than issued in one burst: 48 copies issued at once
+// back up the CU's vector-memory queue and hold every wave at the issue.
+struct PP {
+  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int kThreads = 512;
+  static constexpr int MI = 4, NI = 2, WM = 128, WN = 64, KK = 4;
+  static constexpr int kAElems = BM * BK;
+  static constexpr int kBTPitch = BN + 16;
+  static constexpr int kWSlot = 10240;          // 8 KB packed, 1 KB scales, 1 KB nested scales
+  template <bool TRANS>
+  static constexpr int b_elems() { return TRANS ? BK * kBTPitch : BN * BK; }
+  template <bool TRANS>
+  static constexpr int lds_bytes() { return 2 * kAElems * 2 + 2 * b_elems<TRANS>() * 2 + 2 * kWSlot; }
+};
+static_assert(PP::lds_bytes<true>() + 1024 <= 160 * 1024, "LDS budget of one workgroup");
+
+template <bool TRANS, bool NESTED, bool GROUPED>
+__global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
+  constexpr int BM = PP::BM, BN = PP::BN, BK = PP::BK;
+  constexpr int kBElems = PP::b_elems<TRANS>();
+  constexpr int kBOff = 2 * PP::kAElems * 2;
+  constexpr int kWOff = kBOff + 2 * kBElems * 2;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ float sncode[256];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t N = p.w.N, K = p.w.K;
+  const int64_t Nc = TRANS ? K : N;
+  const int64_t Kc = TRANS ? N : K;
+  const int ktiles = static_cast<int>((Kc + BK - 1) / BK);
+
+  // ---- tile owned by this workgroup (as k_gemm) ----------------------------------
+  const int tt = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = tt % p.m_tiles;
+  const int cz = tt / p.m_tiles;
+  const int z = cz % p.splits;
+  const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
+  int64_t row0, row_end, wrow_base = 0;
+  if constexpr (GROUPED) {
+    int acc = 0, e_found = -1;
+    int64_t lo = 0, hi = 0;
+    for (int e = 0; e < p.E; ++e) {
+      int64_t a = p.offsets[e], b = p.offsets[e + 1];
+      a = a < 0 ? 0 : (a > p.M ? p.M : a);
+      b = b < a ? a : (b > p.M ? p.M : b);
+      const int cnt = static_cast<int>((b - a + BM - 1) / BM);
+      if (mt < acc + cnt) { e_found = e; lo = a + static_cast<int64_t>(mt - acc) * BM; hi = b; break; }
+      acc += cnt;
+    }
+    if (e_found < 0) return;
+    row0 = lo;
+    row_end = hi;
+    wrow_base = static_cast<int64_t>(e_found) * N;
+  } else {
+    row0 = static_cast<int64_t>(mt) * BM;
+    row_end = p.M;
+  }
+  const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
+  const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
+  const int n = ke - kb;
+
+  auto a_tile = [&](int stage) { return lds + stage * PP::kAElems; };
+  auto b_tile = [&](int buf) { return lds + 2 * PP::kAElems + buf * kBElems; };
+  char* const w_area = reinterpret_cast<char*>(lds) + kWOff;
+
+  if constexpr (NESTED) {
+    if (tid < 256) sncode[tid] = p.w.ncode[tid];
+  }
+  float code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
+  const float off = NESTED ? p.w.nested_offset[0] : 0.f;
+
+  // ---- copies (every wave issues its share) ---------------------------------------
+  // activation: wave w copies rows [32w, 32w + 32), 8 rows per instruction
+  const int a_r_in = lane >> 3, a_unit = lane & 7;
+  // j-th of the wave's four activation copy instructions of step i
+  auto issue_a = [&](int i, int stage, int j) {
+    const int kt = kb + (i < n ? i : n - 1);
+    const int64_t c0 = static_cast<int64_t>(kt) * BK;
+    const int r = 32 * wave + 8 * j + a_r_in;
+    int64_t row = row0 + r;
+    row = row < row_end ? row : row_end - 1;
+    int64_t col = c0 + 8 * swz(r, a_unit);
+    col = col < Kc ? col : Kc - 8;
+    __builtin_amdgcn_global_load_lds(p.A + row * Kc + col,
+                                     (lds_void_t*)(a_tile(stage) + (32 * wave + 8 * j) * BK), 16, 0, 0);
+  };
+  // weights: thread t expands half h = t & 1 of unit u = t >> 1 of the step
+  // (fwd: W row col0 + u, block kt; bwd: W row kt*64 + u % 64, block
+  // col0/64 + u / 64).  Lane t of the packed copy fetches exactly those 16
+  // bytes.  The scales of units 64v .. 64v+63 are copied by wave v (v < 4),
+  // their nested scales by wave v + 4, one unit per lane.
+  struct UnitG {
+    int64_t off0;
+    int var_in;
+    bool fixed_ok;
+  };
+  const int64_t dstep = TRANS ? static_cast<int64_t>(BK) * K : BK;
+  const int64_t var_lim = TRANS ? N : K;
+  auto unit_of = [&](int uu) {
+    UnitG g;
+    if constexpr (TRANS) {
+      const int64_t wcol = col0 + 64 * (uu / 64);
+      g.fixed_ok = wcol < K;
+      g.off0 = (wrow_base + uu % 64) * K + wcol;
+      g.var_in = uu % 64;
+    } else {
+      const int64_t wrow = col0 + uu;
+      g.fixed_ok = wrow < N;
+      g.off0 = (wrow_base + wrow) * K;
+      g.var_in = 0;
+    }
+    return g;
+  };
+  const int u = tid >> 1, hh = tid & 1;
+  const UnitG own = unit_of(u);
+  const UnitG scu = unit_of(64 * (wave & 3) + lane);     // unit whose scale this lane copies
+  auto unit_valid = [&](const UnitG& g, int kt) {
+    return g.fixed_ok & (static_cast<int64_t>(kt) * BK + g.var_in < var_lim);
+  };
+  auto unit_flat = [&](const UnitG& g, int kt) -> uint64_t {
+    return unit_valid(g, kt) ? static_cast<uint64_t>(g.off0 + kt * dstep) : 0;   // multiple of 64
+  };
+  auto issue_wpk = [&](int i, int slot) {
+    const int kt = kb + (i < n ? i : n - 1);
+    char* sl = w_area + slot * PP::kWSlot;
+    // (a named pointer: with this expression inline in the call, the host
+    // compilation pass silently drops the kernel's launch stub)
+    const uint8_t* src = p.w.packed + (unit_flat(own, kt) >> 1) + 16 * hh;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + 1024 * wave), 16, 0, 0);
+  };
+  auto issue_ws = [&](int i, int slot) {
+    const int kt = kb + (i < n ? i : n - 1);
+    char* sl = w_area + slot * PP::kWSlot;
+    const uint64_t b = unit_flat(scu, kt) >> 6;
+    if (wave < 4) {
+      if constexpr (NESTED) {
+        // one byte per lane, written zero-extended to the lane's dword
+        __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.w.absmax) + b,
+                                         (lds_void_t*)(sl + 8192 + 256 * wave), 1, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(static_cast<const float*>(p.w.absmax) + b,
+                                         (lds_void_t*)(sl + 8192 + 256 * wave), 4, 0, 0);
+      }
+    } else if constexpr (NESTED) {
+      __builtin_amdgcn_global_load_lds(p.w.nested_absmax + (b >> 8),
+                                       (lds_void_t*)(sl + 9216 + 256 * (wave - 4)), 4, 0, 0);
+    }
+  };
+  const uint32_t st_pk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) + 16 * tid;
+  const uint32_t st_sc = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) + 8192 + 4 * u;
+  const uint32_t st_ncode = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)sncode));
+  struct Staged {
+    u32x4_t pk;
+    uint32_t sc, s2;
+  };
+#define NF4_PP_READ(OFF)                                                                   \
+  asm volatile("ds_read_b128 %0, %3 offset:" #OFF "\n\t"                                   \
+               "ds_read_b32 %1, %4 offset:" #OFF "\n\t"                                    \
+               "ds_read_b32 %2, %4 offset:" #OFF "+1024\n\t"                               \
+               "s_waitcnt lgkmcnt(0)"                                                      \
+               : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)                                        \
+               : "v"(st_pk), "v"(st_sc)                                                    \
+               : "memory")
+  auto read_unit = [&](int slot) {
+    Staged r;
+    static_assert(PP::kWSlot == 10240, "slot offsets below");
+    if (slot == 0) NF4_PP_READ(0);
+    else NF4_PP_READ(10240);
+    return r;
+  };
+#undef NF4_PP_READ
+  auto b_dst = [&](int buf, int d) -> uint16_t* {
+    if constexpr (TRANS) {
+      return b_tile(buf) + (u % 64) * PP::kBTPitch + 64 * (u / 64) + 32 * hh + 8 * d;
+    } else {
+      return b_tile(buf) + u * BK + 8 * swz(u, 4 * hh + d);
+    }
+  };
+  // the copies of step `ci` issued from inside the first phase of a step:
+  // group g of that phase issues activation copy g, plus the weight copy
+  // (g == 1) and the scale copy (g == 2)
+  int ci = 0;
+  auto dma = [&](int g) {
+    issue_a(ci + 1, (ci + 1) & 1, g);
+    if (g == 1) issue_wpk(ci + 2, ci & 1);
+    if (g == 2) issue_ws(ci + 2, ci & 1);
+  };
+  auto expand = [&](int i, int slot, int buf, bool with_dma) {
+    const int kt = kb + (i < n ? i : n - 1);
+    const bool valid = unit_valid(own, kt);
+    const Staged r = read_unit(slot);
+    float a;
+    if constexpr (NESTED) {
+      float nc;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(nc) : "v"(st_ncode + 4 * (r.sc & 0xFF)) : "memory");
+      a = __fadd_rn(__fmul_rn(nc, __uint_as_float(r.s2)), off);
+    } else {
+      a = __uint_as_float(r.sc);
+    }
+    // an invalid unit copied unit 0 of the tensor; a zero scale makes every
+    // one of its weights zero
+    const Lut lt = make_lut(code, valid ? a : 0.f);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t o[4];
+      expand8(r.pk[d], lt, o);
+      *reinterpret_cast<u32x4_t*>(b_dst(buf, d)) = u32x4_t{o[0], o[1], o[2], o[3]};
+      if (with_dma) dma(d);
+    }
+  };
+
+  // ---- MFMA part ------------------------------------------------------------------
+  const int wm = wave >> 2, wn = wave & 3;
+  const int r32 = lane & 31, h = lane >> 5;
+  f32x16_t acc[PP::MI][PP::NI];
+#pragma unroll
+  for (int i = 0; i < PP::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < PP::NI; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int y = h ^ ((r32 >> 1) & 7);
+  const char* pa[4];
+  const char* pb[4];
+  {
+    const char* a0 = reinterpret_cast<const char*>(lds) + (wm * PP::WM + r32) * BK * 2;
+    const char* b0 = reinterpret_cast<const char*>(lds) + kBOff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pa[q] = a0 + 16 * ((2 * q) ^ y);
+      if constexpr (TRANS) {
+        const int tg = lane >> 4, ts = lane & 15;
+        const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+        const int tr_col = wn * PP::WN + 16 * (tg & 1) + 4 * (ts & 3);
+        pb[q] = b0 + (tr_row * PP::kBTPitch + tr_col) * 2;
+      } else {
+        pb[q] = b0 + (wn * PP::WN + r32) * BK * 2 + 16 * ((2 * q) ^ y);
+      }
+    }
+  }
+  struct Frags {
+    bf16x8_t a[PP::MI];
+    bf16x8_t b[PP::NI];
+  };
+  auto load_frags = [&](int stage, int buf, int kk, Frags& f) {
+#pragma unroll
+    for (int i = 0; i < PP::MI; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8_t*>(pa[kk & 3] + stage * PP::kAElems * 2 + i * 32 * BK * 2);
+#pragma unroll
+    for (int j = 0; j < PP::NI; ++j) {
+      if constexpr (TRANS) {
+        const char* src = pb[0] + buf * kBElems * 2 + (16 * kk * PP::kBTPitch + 32 * j) * 2;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * PP::kBTPitch * 2));
+        u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
+        f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
+      } else {
+        f.b[j] = *reinterpret_cast<const bf16x8_t*>(pb[kk & 3] + buf * kBElems * 2 + j * 32 * BK * 2);
+      }
+    }
+  };
+  auto compute = [&](int stage, int buf, bool with_dma) {
+    Frags f0, f1;
+    load_frags(stage, buf, 0, f0);
+#pragma unroll
+    for (int kk = 0; kk < PP::KK; ++kk) {
+      Frags& fc = (kk & 1) ? f1 : f0;
+      Frags& fn = (kk & 1) ? f0 : f1;
+      if (kk + 1 < PP::KK) load_frags(stage, buf, kk + 1, fn);
+#pragma unroll
+      for (int i = 0; i < PP::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < PP::NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+      if (with_dma) dma(kk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- pipeline -------------------------------------------------------------------
+  // Step i multiplies stage/buffer i % 2 and expands step i+1 into the other
+  // buffer.  At its start every wave issues the activation copy of step i+1
+  // and the weight copy of step i+2; all of them must have landed by the end
+  // of the step (vmcnt(0)), then one barrier.
+  auto wait_vm = [](auto cnt) {
+    constexpr int c = decltype(cnt)::value;
+    __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | (7 << 4));
+  };
+  auto end_step = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    wait_vm(ic<0>{});
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const bool mfma_first = wave < 4;
+  if (n > 0) {
+    if constexpr (NESTED) __syncthreads();         // sncode filled
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue_a(0, 0, j);
+    issue_wpk(0, 0);
+    issue_ws(0, 0);
+    issue_wpk(1, 1);
+    issue_ws(1, 1);
+    wait_vm(ic<0>{});
+    __syncthreads();                               // every wave's copies of steps 0 and 1 landed
+    expand(0, 0, 0, false);
+    __syncthreads();
+    auto step = [&](int i, auto ph) {
+      constexpr int P = decltype(ph)::value;
+      ci = i;
+      // the multiply is not duplicated across the two orders: only the
+      // expansion's position depends on the wave; the copies go with the
+      // first phase
+      if (!mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, true);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(P & 1, P & 1, mfma_first);
+      __builtin_amdgcn_sched_barrier(0);
+      if (mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, false);
+      end_step();
+    };
+    int i = 0;
+    for (; i + 2 <= n; i += 2) {
+      step(i, ic<0>{});
+      step(i + 1, ic<1>{});
+    }
+    if (i < n) step(i, ic<0>{});
+  }
+
+  // ---- epilogue -------------------------------------------------------------------
+#pragma unroll
+  for (int i = 0; i < PP::MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < PP::NI; ++j) {
+      const int64_t col = col0 + wn * PP::WN + 32 * j + r32;
+      if (col >= Nc) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + wm * PP::WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row >= row_end) continue;
+        if (p.splits == 1) {
+          p.C[row * Nc + col] = to_bf16(acc[i][j][v]);
+        } else {
+          p.partial[(static_cast<int64_t>(z) * p.M + row) * Nc + col] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
 // Fixed-order sum of split partials: out = bf16(sum_{s=0}^{S-1} part[s]).
 // Four outputs per thread; n % 4 tails handled one by one.
 __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restrict__ part,
@@ -616,6 +985,25 @@ hipError_t launch_tiled(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hi
   return hipGetLastError();
 }
 
+template <bool TRANS, bool NESTED, bool GROUPED>
+hipError_t launch_pp(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
+  auto kern = k_pp<TRANS, NESTED, GROUPED>;
+  constexpr int lds = PP::lds_bytes<TRANS>();
+  static const bool attr_done = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)attr_done;
+  GemmParams q = p;
+  q.m_tiles = static_cast<int32_t>(m_tiles);
+  const int64_t tiles = ((n_cols + PP::BN - 1) / PP::BN) * m_tiles * p.splits;
+  if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kern<<<dim3(static_cast<unsigned>(tiles)), PP::kThreads, lds, stream>>>(q);
+  return hipGetLastError();
+}
+
 template <bool TRANS, bool GROUPED>
 hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_tiles,
                          int64_t n_cols, hipStream_t stream) {
@@ -624,6 +1012,10 @@ hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_t
   if (bm == BMV && bn == BNV && c == CV) {                                                           \
     return nested ? launch_tiled<BMV, BNV, TRANS, true, GROUPED, CV>(p, m_tiles, n_cols, stream)     \
                   : launch_tiled<BMV, BNV, TRANS, false, GROUPED, CV>(p, m_tiles, n_cols, stream);   \
+  }
+  if (bm == 256 && bn == 256 && c == 0) {
+    return nested ? launch_pp<TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
+                  : launch_pp<TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
   }
   NF4_CASE(256, 256, 2)
   NF4_CASE(128, 256, 1)
@@ -687,15 +1079,30 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   if (o_bm == 64 || o_bm == 128 || o_bm == 256) pl.bm = o_bm;
   if (o_bn == 128 || o_bn == 256) pl.bn = o_bn;
   if (pl.bm == 256) pl.bn = 256;                   // 256 x 128 at BK 128 exceeds the LDS
-  pl.consumers = (pl.bm == 256) ? 2 : 1;           // 256-row tiles: 8 consumer waves
+  // 256 x 256 runs the ping-pong kernel (consumers = 0); NF4_CONSUMERS=2
+  // selects the producer/consumer kernel with 8 MFMA waves instead
+  pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : 0) : 1;
   if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
   const int bk = 16384 / pl.bn;
   const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + pl.bn - 1) / pl.bn);
   const int64_t ksteps = (kc + bk - 1) / bk;
+  // Split count: minimise (rounds of workgroups over the compute units) x
+  // (steps per workgroup) x step time + the fixed-order reduction, which
+  // moves (4 S + 2) M Nc bytes.  Step time is modelled at ~3.8 TFLOP/s per
+  // compute unit and the reduction at ~5 TB/s; each split keeps >= 8 steps.
   int s = 1;
-  // Split the contraction only while fewer than half the compute units have a
-  // tile, keeping at least 512 of the contraction per split.
-  while (tiles * s * 2 <= cus && (ksteps * bk) / (2 * s) >= 512 && s < 8) s *= 2;
+  {
+    const double t_step = 2.0 * pl.bm * pl.bn * bk / 3.8e6;                  // us
+    double best = 0;
+    for (int c = 1; c <= 8; ++c) {
+      if (c > 1 && ksteps < 8 * c) break;
+      const int64_t rounds = (tiles * c + cus - 1) / cus;
+      const int64_t steps = (ksteps + c - 1) / c;
+      double t = static_cast<double>(rounds) * static_cast<double>(steps) * t_step;
+      if (c > 1) t += (4.0 * c + 2.0) * static_cast<double>(M) * static_cast<double>(nc) / 5.0e6;
+      if (c == 1 || t < best) { best = t; s = c; }
+    }
+  }
   if (o_s >= 1 && o_s <= 16) s = o_s;
   pl.splits = s;
   pl.ws_bytes = (s > 1) ? static_cast<size_t>(s) * static_cast<size_t>(M) * static_cast<size_t>(nc) * 4 : 0;
@@ -711,7 +1118,7 @@ GemmPlan plan_grouped(GemmKind, int64_t total_M, int64_t, int64_t, int32_t E) {
   // rows per expert are only known on the device; size the tile by the mean
   const int64_t mean = (E > 0) ? (total_M + E - 1) / E : total_M;
   pl.bm = (mean <= 96) ? 64 : (mean <= 192 ? 128 : 256);
-  pl.consumers = (pl.bm == 256) ? 2 : 1;
+  pl.consumers = (pl.bm == 256) ? 0 : 1;
   return pl;
 }
 

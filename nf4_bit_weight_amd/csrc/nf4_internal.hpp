@@ -37,7 +37,8 @@ enum class GemmKind { kFwd, kBwdInput };
 struct GemmPlan {
   int bm;          // rows of the activation tile
   int bn;          // output columns per tile (256 or 128)
-  int consumers;   // MFMA waves per SIMD (1 or 2) beside one expanding wave
+  int consumers;   // MFMA waves per SIMD (1 or 2) beside one expanding wave;
+                   // 0 = the 256 x 256 ping-pong kernel
   int splits;      // contraction split count (1 = none)
   bool small_m;    // weight-streaming forward (bm = MFMA rows 16 / 32)
   int kc;          // weight-streaming forward: contraction per split
