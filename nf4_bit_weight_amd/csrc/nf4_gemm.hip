@@ -576,10 +576,14 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
 // with double-buffered MFMA fragments (at two waves per SIMD every wave has
 // 256 VGPRs, room the three-waves-per-SIMD producer/consumer layout lacks),
 // and every thread also expands half a weight unit (32 weights) per step.
-// The two waves sharing a SIMD (w and w + 4) run the step's two halves in
-// opposite order -- waves 0-3 multiply, then expand; waves 4-7 expand, then
-// multiply -- so the expansion VALU of one runs under the MFMAs of the other
-// (measured: another wave's VALU leaves MFMA throughput intact).
+// Two schedules for a step, picked per direction by measurement:
+//   forward: each k-step's 8 MFMAs are interleaved with one piece of the
+//            next step's expansion (scheduling groups of one MFMA and a few
+//            VALU operations), so every wave mixes both;
+//   input gradient: the waves sharing a SIMD (w and w + 4; measured: this is
+//            how the CU places them) take the multiply and expand halves in
+//            opposite order, one wave's expansion under the other's MFMAs
+//            (measured: another wave's VALU leaves MFMA throughput intact).
 // Staging as in k_gemm: LDS-direct copies of the activation tile (2 stages)
 // and of the packed weights and scales (2 slots), one explicit vmcnt per
 // step, one barrier per step.  A wave's six copy instructions of a step are
@@ -661,17 +665,26 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   // ---- copies (every wave issues its share) ---------------------------------------
   // activation: wave w copies rows [32w, 32w + 32), 8 rows per instruction
   const int a_r_in = lane >> 3, a_unit = lane & 7;
-  // j-th of the wave's four activation copy instructions of step i
-  auto issue_a = [&](int i, int stage, int j) {
-    const int kt = kb + (i < n ? i : n - 1);
-    const int64_t c0 = static_cast<int64_t>(kt) * BK;
+  // j-th of the wave's four activation copy instructions of step i.  The
+  // row part of each lane's address is fixed for the workgroup (rows past the
+  // end clamped); per step only the column moves.
+  const uint16_t* a_row_ptr[4];
+  int a_colofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
     const int r = 32 * wave + 8 * j + a_r_in;
     int64_t row = row0 + r;
     row = row < row_end ? row : row_end - 1;
-    int64_t col = c0 + 8 * swz(r, a_unit);
+    a_row_ptr[j] = p.A + row * Kc;
+    a_colofs[j] = 8 * swz(r, a_unit);
+  }
+  auto issue_a = [&](int i, int stage, int j) __attribute__((always_inline)) {
+    const int kt = kb + (i < n ? i : n - 1);
+    const int64_t c0 = static_cast<int64_t>(kt) * BK;
+    int64_t col = c0 + a_colofs[j];
     col = col < Kc ? col : Kc - 8;
-    __builtin_amdgcn_global_load_lds(p.A + row * Kc + col,
-                                     (lds_void_t*)(a_tile(stage) + (32 * wave + 8 * j) * BK), 16, 0, 0);
+    const uint16_t* src = a_row_ptr[j] + col;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(a_tile(stage) + (32 * wave + 8 * j) * BK), 16, 0, 0);
   };
   // weights: thread t expands half h = t & 1 of unit u = t >> 1 of the step
   // (fwd: W row col0 + u, block kt; bwd: W row kt*64 + u % 64, block
@@ -709,15 +722,16 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   auto unit_flat = [&](const UnitG& g, int kt) -> uint64_t {
     return unit_valid(g, kt) ? static_cast<uint64_t>(g.off0 + kt * dstep) : 0;   // multiple of 64
   };
-  auto issue_wpk = [&](int i, int slot) {
+  // packed bytes of this thread's half unit: a fixed lane base plus the
+  // uniform step offset kt * dstep / 2; invalid units read unit 0
+  const uint8_t* const pk_base = p.w.packed + (own.off0 >> 1) + 16 * hh;
+  auto issue_wpk = [&](int i, int slot) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
     char* sl = w_area + slot * PP::kWSlot;
-    // (a named pointer: with this expression inline in the call, the host
-    // compilation pass silently drops the kernel's launch stub)
-    const uint8_t* src = p.w.packed + (unit_flat(own, kt) >> 1) + 16 * hh;
+    const uint8_t* src = unit_valid(own, kt) ? pk_base + ((static_cast<int64_t>(kt) * dstep) >> 1) : p.w.packed;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + 1024 * wave), 16, 0, 0);
   };
-  auto issue_ws = [&](int i, int slot) {
+  auto issue_ws = [&](int i, int slot) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
     char* sl = w_area + slot * PP::kWSlot;
     const uint64_t b = unit_flat(scu, kt) >> 6;
@@ -750,7 +764,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
                : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)                                        \
                : "v"(st_pk), "v"(st_sc)                                                    \
                : "memory")
-  auto read_unit = [&](int slot) {
+  auto read_unit = [&](int slot) __attribute__((always_inline)) {
     Staged r;
     static_assert(PP::kWSlot == 10240, "slot offsets below");
     if (slot == 0) NF4_PP_READ(0);
@@ -769,12 +783,12 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   // group g of that phase issues activation copy g, plus the weight copy
   // (g == 1) and the scale copy (g == 2)
   int ci = 0;
-  auto dma = [&](int g) {
+  auto dma = [&](int g) __attribute__((always_inline)) {
     issue_a(ci + 1, (ci + 1) & 1, g);
     if (g == 1) issue_wpk(ci + 2, ci & 1);
     if (g == 2) issue_ws(ci + 2, ci & 1);
   };
-  auto expand = [&](int i, int slot, int buf, bool with_dma) {
+  auto expand = [&](int i, int slot, int buf, bool with_dma) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
     const bool valid = unit_valid(own, kt);
     const Staged r = read_unit(slot);
@@ -832,7 +846,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     bf16x8_t a[PP::MI];
     bf16x8_t b[PP::NI];
   };
-  auto load_frags = [&](int stage, int buf, int kk, Frags& f) {
+  auto load_frags = [&](int stage, int buf, int kk, Frags& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PP::MI; ++i)
       f.a[i] = *reinterpret_cast<const bf16x8_t*>(pa[kk & 3] + stage * PP::kAElems * 2 + i * 32 * BK * 2);
@@ -849,7 +863,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       }
     }
   };
-  auto compute = [&](int stage, int buf, bool with_dma) {
+  auto compute = [&](int stage, int buf, bool with_dma) __attribute__((always_inline)) {
     Frags f0, f1;
     load_frags(stage, buf, 0, f0);
 #pragma unroll
@@ -865,6 +879,57 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       if (with_dma) dma(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // One step in a single pass: k-step kk's 8 MFMAs are interleaved with one
+  // piece of the next step's expansion (kk = 0: the byte table; kk > 0: one
+  // 8-weight group), and with one of the wave's copy instructions, so that
+  // every wave keeps both the MFMA pipe and the VALU busy; the scheduling
+  // groups ask for one MFMA followed by a few VALU operations.
+  auto mixed = [&](int i, int stage, int buf_r, int slot_w, int buf_w) __attribute__((always_inline)) {
+    const int kt = kb + (i + 1 < n ? i + 1 : n - 1);
+    const bool valid = unit_valid(own, kt);
+    Frags f0, f1;
+    load_frags(stage, buf_r, 0, f0);
+    const Staged r = read_unit(slot_w);
+    float a;
+    if constexpr (NESTED) {
+      float nc;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(nc) : "v"(st_ncode + 4 * (r.sc & 0xFF)) : "memory");
+      a = __fadd_rn(__fmul_rn(nc, __uint_as_float(r.s2)), off);
+    } else {
+      a = __uint_as_float(r.sc);
+    }
+    Lut lt;
+#pragma unroll
+    for (int kk = 0; kk < PP::KK; ++kk) {
+      Frags& fc = (kk & 1) ? f1 : f0;
+      Frags& fn = (kk & 1) ? f0 : f1;
+      if (kk + 1 < PP::KK) load_frags(stage, buf_r, kk + 1, fn);
+#pragma unroll
+      for (int ii = 0; ii < PP::MI; ++ii)
+#pragma unroll
+        for (int j = 0; j < PP::NI; ++j)
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[ii], fc.b[j], acc[ii][j], 0, 0, 0);
+      if (kk == 0) {
+        lt = make_lut(code, valid ? a : 0.f);
+      } else {
+        uint32_t o[4];
+        expand8(r.pk[kk - 1], lt, o);
+        *reinterpret_cast<u32x4_t*>(b_dst(buf_w, kk - 1)) = u32x4_t{o[0], o[1], o[2], o[3]};
+      }
+      dma(kk);
+#pragma unroll
+      for (int m = 0; m < PP::MI * PP::NI; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t o[4];
+    expand8(r.pk[3], lt, o);
+    *reinterpret_cast<u32x4_t*>(b_dst(buf_w, 3)) = u32x4_t{o[0], o[1], o[2], o[3]};
   };
 
   // ---- pipeline -------------------------------------------------------------------
@@ -897,17 +962,21 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     __syncthreads();                               // every wave's copies of steps 0 and 1 landed
     expand(0, 0, 0, false);
     __syncthreads();
-    auto step = [&](int i, auto ph) {
+    auto step = [&](int i, auto ph) __attribute__((always_inline)) {
       constexpr int P = decltype(ph)::value;
       ci = i;
-      // the multiply is not duplicated across the two orders: only the
-      // expansion's position depends on the wave; the copies go with the
-      // first phase
-      if (!mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, true);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(P & 1, P & 1, mfma_first);
-      __builtin_amdgcn_sched_barrier(0);
-      if (mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, false);
+      if constexpr (!TRANS) {
+        mixed(i, P & 1, P & 1, (P + 1) & 1, (P + 1) & 1);
+      } else {
+        // the input gradient measured faster with the two halves of a step
+        // run as separate phases, in opposite order on the two waves of a
+        // SIMD (w and w + 4): one wave's expansion under the other's MFMAs
+        if (!mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, true);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P & 1, P & 1, mfma_first);
+        __builtin_amdgcn_sched_barrier(0);
+        if (mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, false);
+      }
       end_step();
     };
     int i = 0;

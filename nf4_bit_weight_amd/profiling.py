@@ -27,7 +27,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/nf4_gemm.hip", "csrc/nf4_device.hpp")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-FUSED_KERNELS = ("k_gemm<", "k_splitk_reduce")
+FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_gemv<", "k_splitk_reduce")
 
 
 def kernel_source_sha256() -> str:

@@ -126,3 +126,21 @@ def test_path_counters_host_side(lib):
     assert lib.nf4_path_count(len(L.PATHS)) == -1
     _fwd(lib, x=None)                                         # a rejected call counts nothing
     assert lib.nf4_path_count(2) == 0
+
+
+def test_library_has_no_undefined_internal_symbols():
+    """Every kernel the library launches is defined in it (a kernel whose
+    host-side launch stub is missing would leave an undefined symbol that
+    only fails when the library is loaded on the GPU host)."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    from nf4_bit_weight_amd import _lib
+
+    out = subprocess.run([nm, "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    bad = [ln for ln in out.splitlines() if "nf4" in ln]
+    assert not bad, bad
