@@ -180,6 +180,103 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
     extra["decode_llama8b_fwd"] = dec
 
     log(f"decode done: {dec}")
+
+    # Today's path as the comparator: dequantise every visit, then the dense
+    # bf16 GEMM (hipBLASLt through torch), per Llama projection at M = 512 on
+    # layer 0's weights; and the dense GEMM alone on a resident dequantised
+    # weight (the same-session dense ceiling).  Outputs are compared with the
+    # fused ones: same exact product, different accumulation order.
+    import torch.nn.functional as F
+    M = WL.LLAMA_M
+    comp = {}
+    tot = {"fused_us": 0.0, "dequant_plus_dense_us": 0.0, "dense_only_us": 0.0}
+    for i, p in enumerate(projs):
+        w = llama_weights[0][i]
+        x = WL.gpu_normal_bf16(M, p.K, seed=90_000 + i, device=dev)
+        gy = WL.gpu_normal_bf16(M, p.N, seed=91_000 + i, device=dev)
+        ws_c = workspace_for(torch, api, [p], [M], dev)
+        wd = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=dev)
+        y_f = torch.empty((M, p.N), dtype=torch.bfloat16, device=dev)
+        g_f = torch.empty((M, p.K), dtype=torch.bfloat16, device=dev)
+
+        def fused():
+            api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c)
+            api.nf4_matmul_bwd_input(gy, w, out=g_f, ws=ws_c)
+
+        def today():
+            api.nf4_dequantize(w, out=wd)
+            y = F.linear(x, wd)
+            api.nf4_dequantize(w, out=wd)
+            g = torch.matmul(gy, wd)
+            return y, g
+
+        api.nf4_dequantize(w, out=wd)
+
+        def dense():
+            return F.linear(x, wd), torch.matmul(gy, wd)
+
+        t_f = timed(torch, stream, fused, steps=20, warmup=3) * 1e3
+        t_t = timed(torch, stream, today, steps=20, warmup=3) * 1e3
+        t_d = timed(torch, stream, dense, steps=20, warmup=3) * 1e3
+        api.nf4_reset_path_counts()
+        fused()
+        torch.cuda.synchronize()
+        pc = api.nf4_path_counts()
+        ran_fused = pc["fwd_tiled"] == 1 and pc["bwd_tiled"] == 1
+        y_c, g_c = dense()
+        torch.cuda.synchronize()
+
+        def diff(a, b):
+            a, b = a.float(), b.float()
+            rel = float((a - b).norm().item() / max(b.norm().item(), 1e-30))
+            same = float((a.view(torch.int32) == b.view(torch.int32)).float().mean().item())
+            return rel, same
+
+        ry, ey = diff(y_f, y_c)
+        rg, eg = diff(g_f, g_c)
+        comp[p.name] = {"fused_us": round(t_f, 1), "dequant_plus_dense_us": round(t_t, 1),
+                        "dense_only_us": round(t_d, 1), "speedup_vs_today": round(t_t / t_f, 2),
+                        "fwd_rel_fro_diff": float(f"{ry:.3g}"), "fwd_identical_frac": round(ey, 4),
+                        "bwd_rel_fro_diff": float(f"{rg:.3g}"), "bwd_identical_frac": round(eg, 4),
+                        "fused_kernels_ran": ran_fused}
+        tot["fused_us"] += t_f
+        tot["dequant_plus_dense_us"] += t_t
+        tot["dense_only_us"] += t_d
+        del x, gy, ws_c, wd, y_f, g_f, y_c, g_c
+    flops_layer = 2 * sum(2.0 * M * p.N * p.K for p in projs)
+    comp["layer_total"] = {k: round(v, 1) for k, v in tot.items()}
+    comp["layer_total"]["fused_tflops"] = round(flops_layer / (tot["fused_us"] * 1e-6) / 1e12, 1)
+    comp["layer_total"]["dense_only_tflops"] = round(flops_layer / (tot["dense_only_us"] * 1e-6) / 1e12, 1)
+    comp["layer_total"]["today_tflops"] = round(flops_layer / (tot["dequant_plus_dense_us"] * 1e-6) / 1e12, 1)
+    # decode sizes, forward only: the streaming kernel against dequantise +
+    # dense GEMV/GEMM, summed over layer 0's seven projections
+    for Md in WL.DECODE_MS:
+        t = {"fused_us": 0.0, "dequant_plus_dense_us": 0.0, "dense_only_us": 0.0}
+        rels, ran = [], True
+        for i, p in enumerate(projs):
+            w = llama_weights[0][i]
+            x = WL.gpu_normal_bf16(Md, p.K, seed=92_000 + i, device=dev)
+            ws_c = workspace_for(torch, api, [p], [Md], dev)
+            wd = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=dev)
+            y_f = torch.empty((Md, p.N), dtype=torch.bfloat16, device=dev)
+            t["fused_us"] += timed(torch, stream, lambda: api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c),
+                                   steps=20, warmup=3) * 1e3
+            t["dequant_plus_dense_us"] += timed(
+                torch, stream, lambda: F.linear(x, api.nf4_dequantize(w, out=wd)), steps=20, warmup=3) * 1e3
+            t["dense_only_us"] += timed(torch, stream, lambda: F.linear(x, wd), steps=20, warmup=3) * 1e3
+            api.nf4_reset_path_counts()
+            api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c)
+            y_c = F.linear(x, wd)
+            torch.cuda.synchronize()
+            ran = ran and api.nf4_path_counts()["fwd_small_m"] == 1
+            rels.append(float((y_f.float() - y_c.float()).norm().item() / max(y_c.float().norm().item(), 1e-30)))
+            del x, ws_c, wd, y_f, y_c
+        comp[f"decode_M={Md}_fwd"] = {k: round(v, 1) for k, v in t.items()}
+        comp[f"decode_M={Md}_fwd"].update({
+            "speedup_vs_today": round(t["dequant_plus_dense_us"] / t["fused_us"], 2),
+            "max_rel_fro_diff": float(f"{max(rels):.3g}"), "fused_kernels_ran": ran})
+    extra["comparator_llama8b_layer0"] = comp
+    log(f"comparator done: {comp['layer_total']}")
     # Qwen-32B-shaped layer at M = 2048: two layer copies, rotated
     qp = WL.QWEN_32B
     M = WL.QWEN_M
