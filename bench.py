@@ -277,6 +277,9 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
             "max_rel_fro_diff": float(f"{max(rels):.3g}"), "fused_kernels_ran": ran})
     extra["comparator_llama8b_layer0"] = comp
     log(f"comparator done: {comp['layer_total']}")
+
+    extra["layer_streaming_llama8b_m512"] = run_streaming(torch, api, WL, dev, llama_weights, stream)
+    log(f"streaming done: {extra['layer_streaming_llama8b_m512']}")
     # Qwen-32B-shaped layer at M = 2048: two layer copies, rotated
     qp = WL.QWEN_32B
     M = WL.QWEN_M
@@ -335,6 +338,71 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
         "rows": T,
     }
     return extra
+
+
+def run_streaming(torch, api, WL, dev, llama_weights, stream, slots=3):
+    """The 32-layer step with every layer's NF4 fields copied from page-locked
+    host memory into a ring of device slots on each visit (forward in order,
+    input gradients in reverse: 64 visits), against the same step on resident
+    weights.  Reports tokens/s and the arm's device bytes (persistent weights
+    or slots, plus the step's transient peak) together, the copy-only time of
+    the same visit sequence, and whether the outputs are bit-identical."""
+    from nf4_bit_weight_amd.streaming import LayerBuffer, SlotStreamer
+    projs = WL.LLAMA_8B
+    names = [p.name for p in projs]
+    L, M = len(llama_weights), WL.LLAMA_M
+    host = [LayerBuffer(names, row, pin_memory=True) for row in llama_weights]
+    xs = [WL.gpu_normal_bf16(M, p.K, seed=93_000 + i, device=dev) for i, p in enumerate(projs)]
+    gys = [WL.gpu_normal_bf16(M, p.N, seed=94_000 + i, device=dev) for i, p in enumerate(projs)]
+    ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device=dev) for p in projs]
+    gxs = [torch.empty((M, p.K), dtype=torch.bfloat16, device=dev) for p in projs]
+    ws = workspace_for(torch, api, projs, [M], dev)
+    visits = list(range(L)) + list(reversed(range(L)))
+
+    def fn(v, layer, w):
+        for i, n in enumerate(names):
+            if v < L:
+                api.nf4_matmul_fwd(xs[i], w[n], out=ys[i], ws=ws)
+            else:
+                api.nf4_matmul_bwd_input(gys[i], w[n], out=gxs[i], ws=ws)
+
+    def resident():
+        for v, layer in enumerate(visits):
+            fn(v, layer, dict(zip(names, llama_weights[layer])))
+
+    st = SlotStreamer(host, slots, dev)
+
+    def measure(run, persistent):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        ms = timed(torch, stream, run, steps=3, warmup=1)
+        peak = torch.cuda.max_memory_allocated() - base
+        return ms, persistent + peak
+
+    wbytes = sum(w.nbytes() for row in llama_weights for w in row)
+    ms_r, mem_r = measure(resident, wbytes)
+    resident()
+    y_r, g_r = ys[6].clone(), gxs[0].clone()
+    ms_s, mem_s = measure(lambda: st.run(visits, fn), st.device_bytes)
+    st.run(visits, fn)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ys[6].view(torch.int16), y_r.view(torch.int16)) and
+                torch.equal(gxs[0].view(torch.int16), g_r.view(torch.int16)))
+    ms_c = timed(torch, stream, lambda: st.run(visits, lambda v, l, w: None), steps=3, warmup=1)
+    copied = 2 * sum(h.nbytes for h in host)
+    out = {
+        "slots": slots, "layer_MiB": round(host[0].nbytes / 2 ** 20, 1),
+        "resident_ms_per_step": round(ms_r, 2), "resident_tokens_per_s": round(M / (ms_r * 1e-3), 1),
+        "resident_device_MiB": round(mem_r / 2 ** 20, 1),
+        "streamed_ms_per_step": round(ms_s, 2), "streamed_tokens_per_s": round(M / (ms_s * 1e-3), 1),
+        "streamed_device_MiB": round(mem_s / 2 ** 20, 1),
+        "copy_only_ms_per_step": round(ms_c, 2),
+        "h2d_GBps": round(copied / (ms_c * 1e-3) / 1e9, 1),
+        "bitwise_equal_to_resident": same,
+    }
+    del host, st
+    return out
 
 
 # ---------------------------------------------------------------------------

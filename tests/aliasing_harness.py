@@ -50,65 +50,19 @@ from torch.utils.checkpoint import checkpoint
 
 import workloads as WL
 from nf4_bit_weight_amd import api
-from nf4_bit_weight_amd.api import NF4Weight
 from nf4_bit_weight_amd.autograd import nf4_linear
+from nf4_bit_weight_amd.streaming import LayerBuffer
 
-ALIGN = 256          # byte alignment of every field inside a layer buffer
+ALIGN = 256          # alignment of every dense block inside a layer buffer
 
 
 def _round_up(n: int) -> int:
     return (n + ALIGN - 1) // ALIGN * ALIGN
 
 
-@dataclass
-class FieldSpec:
-    offset: int
-    numel: int
-    dtype: torch.dtype
-
-
-class PackedLayer:
-    """One layer's NF4 fields (packed, absmax, nested absmax, nested offset of
-    every projection) laid out in a single byte buffer, so a slot copy moves
-    the whole layer with one ``copy_``.  The code tables stay outside: they
-    are the same for every layer."""
-
-    def __init__(self, names, weights):
-        self.names = list(names)
-        self.spec = []
-        off = 0
-        for w in weights:
-            fields = []
-            for t in w.tensors()[:4]:
-                if t is None:
-                    fields.append(None)
-                    continue
-                fields.append(FieldSpec(off, t.numel(), t.dtype))
-                off += _round_up(t.numel() * t.element_size())
-            self.spec.append((fields, w.N, w.K))
-        self.nbytes = off
-        self.code, self.nested_code = weights[0].code, weights[0].nested_code
-        self.store = torch.empty(off, dtype=torch.uint8, device=weights[0].packed.device)
-        for w, (fields, _, _) in zip(weights, self.spec):
-            for t, f in zip(w.tensors()[:4], fields):
-                if f is not None:
-                    n = f.numel * t.element_size()
-                    self.store[f.offset:f.offset + n].copy_(t.reshape(-1).view(torch.uint8))
-
-    def views(self, buf: torch.Tensor) -> dict:
-        """NF4Weight per projection whose fields are views into ``buf`` (a
-        buffer of this layer's layout: the store itself or a slot)."""
-        out = {}
-        for name, (fields, N, K) in zip(self.names, self.spec):
-            ts = []
-            for f in fields:
-                if f is None:
-                    ts.append(None)
-                    continue
-                size = f.numel * torch.tensor([], dtype=f.dtype).element_size()
-                ts.append(buf[f.offset:f.offset + size].view(f.dtype))
-            out[name] = NF4Weight(ts[0], ts[1], ts[2], ts[3], self.code, self.nested_code, N, K)
-        return out
+# One layer's NF4 fields in a single byte buffer, so a slot copy moves the
+# whole layer with one copy_; views(buf) rebuilds the projections on a slot.
+PackedLayer = LayerBuffer
 
 
 class DenseLayer:

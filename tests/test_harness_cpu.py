@@ -1,7 +1,8 @@
-"""Host-side checks of the aliasing harness's buffer logic (no GPU).
+"""Host-side checks of the layer-buffer and slot logic (no GPU).
 
-The layer buffer must reproduce every field bit for bit through its views,
-keep every field aligned, and the slot ring must hand out slots round-robin,
+The layer buffer (used by the aliasing harness and the layer streamer) must
+reproduce every field bit for bit through its views and keep every field
+aligned; the harness's slot ring must hand out slots round-robin,
 overwriting the one handed out ``n_slots`` acquires earlier.
 """
 
@@ -9,6 +10,7 @@ import numpy as np
 import torch
 
 import aliasing_harness as AH
+from nf4_bit_weight_amd import streaming
 from nf4_bit_weight_amd.api import NF4Weight
 
 
@@ -40,7 +42,7 @@ def test_packed_layer_roundtrip_and_alignment():
                         continue
                     assert got.dtype == want.dtype and got.shape == want.shape
                     assert torch.equal(got.view(torch.uint8), want.view(torch.uint8))
-                    assert (got.data_ptr() - buf.data_ptr()) % AH.ALIGN == 0
+                    assert (got.data_ptr() - buf.data_ptr()) % streaming.ALIGN == 0
         assert lay.nbytes >= sum(w.nbytes() for w in ws)
 
 
@@ -67,3 +69,12 @@ def test_slot_ring_round_robin():
     assert got[0] is got[2] is got[4] and got[1] is got[3]
     # what a holder of the first slot sees after the later acquires
     assert torch.equal(got[0], src[4]) and torch.equal(got[1], src[3])
+
+
+def test_layer_buffer_rejects_small_or_wrong_buffers():
+    import pytest
+    lay = streaming.LayerBuffer(["a"], [_fake_weight(64, 128, 8)])
+    with pytest.raises(ValueError):
+        lay.views(lay.store[:-1])
+    with pytest.raises(ValueError):
+        lay.views(torch.zeros(lay.nbytes, dtype=torch.int8))

@@ -358,3 +358,77 @@ def test_olmoe_saved_dense_weights():
 def test_unnested_storage_formula():
     assert O.storage_bytes(128 * 256, nested=False) == 128 * 256 // 2 + 4 * 512
     assert O.absmax_count(65) == 2 and O.nested_count(64 * 257) == 2
+
+
+# --- fp4: the same codec with another 16-entry table (Experts PR, "Commit 1"
+# table: nf4 / fp4 share the 4-bit packed path) ---------------------------------
+
+def _e2m1_values():
+    """The 16 values of a float with 1 sign, 2 exponent (bias 1) and 1
+    mantissa bit, decoded from the bit fields (exponent 0 is subnormal)."""
+    out = []
+    for bits in range(16):
+        sign = -1.0 if bits & 8 else 1.0
+        e, m = (bits >> 1) & 3, bits & 1
+        mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+        out.append(sign * mag)
+    return out
+
+
+def test_fp4_table_is_e2m1_over_its_max():
+    import math
+    v = sorted(_e2m1_values(), key=lambda x: (x, math.copysign(1.0, x) > 0))
+    want = (np.array(v, dtype=np.float64) / max(abs(x) for x in v)).astype(F32)
+    got = WL.fp4_code_np()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))   # -0 before +0
+    assert np.signbit(got[7]) and not np.signbit(got[8])
+    assert np.all(np.diff(got.astype(np.float64)) >= 0)
+
+
+def test_fp4_round_trip_on_code_values():
+    """fp32(code[q] * s) with a +-s element per block comes back exactly as a
+    value; the +0 entry comes back as index 7 (-0), equal in value."""
+    g = np.random.default_rng(21)
+    code = WL.fp4_code_np()
+    nb = 200
+    q = g.integers(0, 16, size=(nb, 64))
+    q[:, 3] = g.choice([0, 15], size=nb)
+    s = (g.random(nb) * 3 + 0.01).astype(F32)
+    w = (code[q] * s[:, None]).astype(F32)
+    r = O.quantize_nf4(w.reshape(-1), code=code)
+    assert np.array_equal(r["absmax"], s)
+    got_q = O.unpack_nibbles(r["packed"]).reshape(nb, 64)
+    assert np.array_equal(got_q, np.where(q == 8, 7, q))
+    d = O.dequantize_nf4_f32(r["packed"], r["absmax"], code=code)
+    assert np.array_equal(d, w.reshape(-1))                            # -0 == +0 as values
+
+
+def test_fp4_nearest_value_brute_force_and_bound():
+    g = np.random.default_rng(22)
+    code = WL.fp4_code_np()
+    w = (g.standard_normal(64 * 400) * 0.02).astype(F32)
+    w[::11] = 0.0
+    r = O.quantize_nf4(w, code=code)
+    q = O.unpack_nibbles(r["packed"])
+    t = (w.reshape(-1, 64) / r["absmax"][:, None]).astype(F32).astype(np.float64).reshape(-1)
+    c64 = code.astype(np.float64)
+    best = np.abs(t[:, None] - c64[None, :]).min(axis=1)
+    assert np.array_equal(np.abs(t - c64[q]), best)                   # a nearest value
+    # sign kept: t <= 0 maps to a non-positive code (-0 included), t > 0 to a non-negative one
+    assert np.all(np.signbit(code[q][t <= 0])) and not np.any(np.signbit(code[q][t > 0]))
+    d = O.dequantize_nf4_f32(r["packed"], r["absmax"], code=code).reshape(-1, 64)
+    half_gap = np.diff(c64).max() / 2                                   # (1 - 2/3) / 2
+    assert abs(half_gap - 1 / 6) < 1e-7
+    assert np.all(np.abs(d - w.reshape(-1, 64)) <= half_gap * r["absmax"][:, None] * (1 + 1e-6))
+
+
+def test_nf4_beats_fp4_on_normal_weights():
+    """On N(0, s) weights the NormalFloat levels reconstruct with a lower
+    mean-abs error than the float levels (the reason NF4 is the default)."""
+    g = np.random.default_rng(23)
+    w = (g.standard_normal(64 * 2000) * 0.02).astype(F32)
+    err = {}
+    for name, code in (("nf4", O.nf4_code()), ("fp4", WL.fp4_code_np())):
+        r = O.quantize_nf4(w, code=code)
+        err[name] = np.abs(O.dequantize_nf4_f32(r["packed"], r["absmax"], code=code) - w).mean()
+    assert err["nf4"] < err["fp4"]

@@ -67,10 +67,23 @@ NF4_LEVELS = (
     0.0796, 0.1609, 0.2461, 0.3379, 0.4407, 0.5626, 0.7230, 1.0,
 )
 NESTED_UNIFORM = tuple((2.0 * j - 255.0) / 255.0 for j in range(256))
+# The 4-bit float alternative (fp4, a code-table swap on the same kernels):
+# the 16 values of a 1-sign / 2-exponent / 1-mantissa float, magnitudes
+# {0, 0.5, 1, 1.5, 2, 3, 4, 6}, divided by 6 so the largest is 1, in
+# ascending order with -0 before +0.  The stored 4-bit index is the rank in
+# this table, not the float's bit pattern.
+FP4_LEVELS = (
+    -1.0, -4 / 6, -3 / 6, -2 / 6, -1.5 / 6, -1 / 6, -0.5 / 6, -0.0,
+    0.0, 0.5 / 6, 1 / 6, 1.5 / 6, 2 / 6, 3 / 6, 4 / 6, 1.0,
+)
 
 
 def nf4_code_np() -> np.ndarray:
     return np.array(NF4_LEVELS, dtype=np.float64).astype(np.float32)
+
+
+def fp4_code_np() -> np.ndarray:
+    return np.array(FP4_LEVELS, dtype=np.float64).astype(np.float32)
 
 
 def nested_code_np() -> np.ndarray:
