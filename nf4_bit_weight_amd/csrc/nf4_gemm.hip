@@ -1008,6 +1008,309 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Forward, 256 x 256, with the expanded weights kept in registers.
+//
+// The eight waves split the tile by columns only: wave w owns output columns
+// (W rows) 32w .. 32w+31 for all 256 rows, 8 accumulators of 32x32.  Lane l
+// expands W row 32w + l%32, half h = l/32 of the step's 64-block, i.e. 32
+// consecutive weights = one 16-byte load = the MFMA B operands of all four
+// 16-deep k slices of the step: slice kk pairs lane half h with contraction
+// indices 32h + 8kk .. +7, and the activation fragments are read with the
+// same pairing (any fixed assignment of contraction indices to the two lane
+// halves gives the same sum).  No weight tile goes through LDS, so LDS holds
+// a 3-deep activation ring (each copy has two steps to land) and a 3-deep
+// ring of per-wave weight slots, which only the wave that copied them reads.
+// One barrier per step: every wave's activation copy of step i has landed
+// (own vmcnt, then the barrier) and every wave has finished reading the
+// stage that the step's new copy overwrites.
+struct RB {
+  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int kThreads = 512;
+  static constexpr int kStages = 3;
+  static constexpr int kAElems = BM * BK;              // bf16 per activation stage (32 KB)
+  static constexpr int kWWave = 1536;                  // per wave: 1 KB packed, 256 B scale, 256 B nested
+  static constexpr int kWSlot = 8 * kWWave;            // 12 KB
+  static constexpr int kWOff = kStages * kAElems * 2;  // 96 KB
+  static constexpr int kLds = kWOff + kStages * kWSlot;
+};
+static_assert(RB::kLds + 1024 <= 160 * 1024, "LDS budget of one workgroup");
+
+template <bool NESTED, bool GROUPED>
+__global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
+  constexpr int BM = RB::BM, BN = RB::BN, BK = RB::BK;
+  // per-wave copy instructions of one step: 4 activation, packed, scale (+ nested)
+  constexpr int kCopies = NESTED ? 7 : 6;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ float sncode[256];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t N = p.w.N, K = p.w.K;
+  const int ktiles = static_cast<int>((K + BK - 1) / BK);
+
+  const int tt = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = tt % p.m_tiles;
+  const int cz = tt / p.m_tiles;
+  const int z = cz % p.splits;
+  const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
+  int64_t row0, row_end, wrow_base = 0;
+  if constexpr (GROUPED) {
+    int acc = 0, e_found = -1;
+    int64_t lo = 0, hi = 0;
+    for (int e = 0; e < p.E; ++e) {
+      int64_t a = p.offsets[e], b = p.offsets[e + 1];
+      a = a < 0 ? 0 : (a > p.M ? p.M : a);
+      b = b < a ? a : (b > p.M ? p.M : b);
+      const int cnt = static_cast<int>((b - a + BM - 1) / BM);
+      if (mt < acc + cnt) { e_found = e; lo = a + static_cast<int64_t>(mt - acc) * BM; hi = b; break; }
+      acc += cnt;
+    }
+    if (e_found < 0) return;
+    row0 = lo;
+    row_end = hi;
+    wrow_base = static_cast<int64_t>(e_found) * N;
+  } else {
+    row0 = static_cast<int64_t>(mt) * BM;
+    row_end = p.M;
+  }
+  const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
+  const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
+  const int n = ke - kb;
+
+  if constexpr (NESTED) {
+    if (tid < 256) sncode[tid] = p.w.ncode[tid];
+  }
+  float code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
+  const float off = NESTED ? p.w.nested_offset[0] : 0.f;
+
+  // ---- activation copies: wave w copies rows 32w .. 32w+31, 8 rows per
+  // instruction, 16-byte units swizzled (swz) as the fragment reads expect
+  const int a_r_in = lane >> 3, a_unit = lane & 7;
+  const uint16_t* a_row_ptr[4];
+  int a_colofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + 8 * j + a_r_in;
+    int64_t row = row0 + r;
+    row = row < row_end ? row : row_end - 1;
+    a_row_ptr[j] = p.A + row * K;
+    a_colofs[j] = 8 * swz(r, a_unit);
+  }
+  auto stage_ptr = [&](int stage) { return lds + stage * RB::kAElems; };
+  auto issue_a = [&](int i, int stage) __attribute__((always_inline)) {
+    const int kt = kb + (i < n ? i : n - 1);
+    const int64_t c0 = static_cast<int64_t>(kt) * BK;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int64_t col = c0 + a_colofs[j];
+      col = col < K ? col : K - 8;
+      const uint16_t* src = a_row_ptr[j] + col;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_ptr(stage) + (32 * wave + 8 * j) * BK), 16, 0, 0);
+    }
+  };
+
+  // ---- weight copies: lane l fetches the 16 bytes it expands (W row
+  // col0 + 32w + l%32, half l/32 of block kt), that row's block scale and, when
+  // nested, the scale's nested scale, into the wave's part of a slot
+  const int r32 = lane & 31, h = lane >> 5;
+  const int64_t wrow = col0 + 32 * wave + r32;
+  const bool row_ok = wrow < N;
+  const int64_t wrow_g = wrow_base + wrow;
+  const uint8_t* const pk_base = p.w.packed + ((wrow_g * K) >> 1) + 16 * h;
+  const int64_t blocks_per_row = K / BK;
+  char* const w_area = reinterpret_cast<char*>(lds) + RB::kWOff;
+  auto issue_w = [&](int i, int slot) __attribute__((always_inline)) {
+    const int kt = kb + (i < n ? i : n - 1);
+    char* sl = w_area + slot * RB::kWSlot + wave * RB::kWWave;
+    const uint8_t* src = row_ok ? pk_base + static_cast<int64_t>(kt) * (BK / 2) : p.w.packed;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)sl, 16, 0, 0);
+    const int64_t b = row_ok ? wrow_g * blocks_per_row + kt : 0;
+    if constexpr (NESTED) {
+      const uint8_t* sa = static_cast<const uint8_t*>(p.w.absmax) + b;
+      __builtin_amdgcn_global_load_lds(sa, (lds_void_t*)(sl + 1024), 1, 0, 0);
+      const float* sn = p.w.nested_absmax + (b >> 8);
+      __builtin_amdgcn_global_load_lds(sn, (lds_void_t*)(sl + 1280), 4, 0, 0);
+    } else {
+      const float* sa = static_cast<const float*>(p.w.absmax) + b;
+      __builtin_amdgcn_global_load_lds(sa, (lds_void_t*)(sl + 1024), 4, 0, 0);
+    }
+  };
+  const uint32_t st_pk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) +
+                         wave * RB::kWWave + 16 * lane;
+  const uint32_t st_sc = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) +
+                         wave * RB::kWWave + 1024 + 4 * lane;
+  const uint32_t st_ncode = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)sncode));
+  struct Staged {
+    u32x4_t pk;
+    uint32_t sc, s2;
+  };
+#define NF4_RB_READ(OFF)                                                                   \
+  asm volatile("ds_read_b128 %0, %3 offset:" #OFF "\n\t"                                   \
+               "ds_read_b32 %1, %4 offset:" #OFF "\n\t"                                    \
+               "ds_read_b32 %2, %4 offset:" #OFF "+256\n\t"                                \
+               "s_waitcnt lgkmcnt(0)"                                                      \
+               : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)                                        \
+               : "v"(st_pk), "v"(st_sc)                                                    \
+               : "memory")
+  auto read_unit = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    static_assert(RB::kWSlot == 12288, "slot offsets below");
+    Staged r;
+    if constexpr (slot == 0) NF4_RB_READ(0);
+    else if constexpr (slot == 1) NF4_RB_READ(12288);
+    else NF4_RB_READ(24576);
+    if constexpr (!NESTED) r.s2 = 0;
+    return r;
+  };
+#undef NF4_RB_READ
+  auto unit_scale = [&](const Staged& r) __attribute__((always_inline)) {
+    float a;
+    if constexpr (NESTED) {
+      float nc;
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(nc) : "v"(st_ncode + 4 * (r.sc & 0xFF)) : "memory");
+      a = __fadd_rn(__fmul_rn(nc, __uint_as_float(r.s2)), off);
+    } else {
+      a = __uint_as_float(r.sc);
+    }
+    return row_ok ? a : 0.f;     // rows past N expand to zero
+  };
+
+  // ---- MFMA operands ---------------------------------------------------------------
+  f32x16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+  // activation fragment of slice kk, row block mi: row 32mi + r32, logical
+  // 16-byte unit 4h + kk (contraction 32h + 8kk .. +7), stored at unit ^ swz
+  int a_ofs[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) a_ofs[kk] = r32 * BK * 2 + 16 * swz(r32, 4 * h + kk);
+  auto load_a = [&](int stage, int kk, bf16x8_t (&f)[8]) __attribute__((always_inline)) {
+    const char* base = reinterpret_cast<const char*>(stage_ptr(stage)) + a_ofs[kk];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) f[mi] = *reinterpret_cast<const bf16x8_t*>(base + mi * 32 * BK * 2);
+  };
+  bf16x8_t bw[4];      // B operands of the step being multiplied, slice kk in bw[kk]
+
+  // s_waitcnt on vmcnt only (expcnt and lgkmcnt fields at their maximum)
+  auto wait_vm = [](auto cnt) {
+    constexpr int c = decltype(cnt)::value;
+    __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | (7 << 4) | (15 << 8));
+  };
+
+  // ---- pipeline ---------------------------------------------------------------------
+  // Copies of step j: activation in the step j-2 issue, weights in the step
+  // j-3 issue; step i's issue goes out right after its barrier.
+  if (n > 0) {
+    if constexpr (NESTED) __syncthreads();         // sncode filled, before any copy is in flight
+    issue_w(0, 0);
+    issue_a(0, 0);
+    issue_w(1, 1);
+    issue_a(1, 1);
+    issue_w(2, 2);
+    wait_vm(ic<2 * kCopies>{});                    // weights of step 0 landed
+    {
+      const Staged r = read_unit(ic<0>{});
+      const Lut lt = make_lut(code, unit_scale(r));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t o[4];
+        expand8(r.pk[d], lt, o);
+        bw[d] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+      }
+    }
+
+    // Step i: the activation fragments of slice 0 were read at the end of
+    // step i-1; slice kk's 8 MFMAs run with the reads of slice kk+1 in flight
+    // and, interleaved, one piece of step i+1's expansion.  After the last
+    // MFMAs are issued the wave waits for its part of A(i+1), joins the
+    // barrier and reads slice 0 of step i+1 while those MFMAs still run.
+    bf16x8_t f0[8], f1[8];
+    wait_vm(ic<2 * kCopies - 4>{});                // own part of A(0) landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    load_a(0, 0, f0);
+    auto step = [&](int i, auto ph) __attribute__((always_inline)) {
+      constexpr int P = decltype(ph)::value;       // i % 3
+      __builtin_amdgcn_sched_barrier(0);
+      issue_a(i + 2, (P + 2) % 3);
+      issue_w(i + 3, P);
+      wait_vm(ic<2 * kCopies>{});                  // weights of step i+1 landed (batch i-2 done)
+      asm volatile("" ::: "memory");
+      const Staged r = read_unit(ic<(P + 1) % 3>{});
+      Lut lt;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t (&fc)[8] = (kk & 1) ? f1 : f0;
+        bf16x8_t (&fn)[8] = (kk & 1) ? f0 : f1;
+        if (kk + 1 < 4) load_a(P, kk + 1, fn);
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi)
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[mi], bw[kk], acc[mi], 0, 0, 0);
+        if (kk == 0) {
+          lt = make_lut(code, unit_scale(r));
+        } else {
+          uint32_t o[4];
+          expand8(r.pk[kk - 1], lt, o);
+          bw[kk - 1] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        uint32_t o[4];
+        expand8(r.pk[3], lt, o);
+        bw[3] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      // A(i+1) was the first part of batch i-1: W(i+2) of that batch and all
+      // of batch i may still be in flight
+      wait_vm(ic<kCopies + kCopies - 4>{});
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      load_a((P + 1) % 3, 0, f0);                  // slice 0 of step i+1 (a re-read on the last step)
+    };
+    int i = 0;
+    for (; i + 3 <= n; i += 3) {
+      step(i, ic<0>{});
+      step(i + 1, ic<1>{});
+      step(i + 2, ic<2>{});
+    }
+    if (i < n) step(i, ic<0>{});
+    if (i + 1 < n) step(i + 1, ic<1>{});
+    wait_vm(ic<0>{});                              // no copy outlives the workgroup
+  }
+
+  // ---- epilogue -----------------------------------------------------------------------
+  const int64_t col = col0 + 32 * wave + r32;
+  if (col < N) {
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row >= row_end) continue;
+        if (p.splits == 1) {
+          p.C[row * N + col] = to_bf16(acc[mi][v]);
+        } else {
+          p.partial[(static_cast<int64_t>(z) * p.M + row) * N + col] = acc[mi][v];
+        }
+      }
+    }
+  }
+}
+
 // Fixed-order sum of split partials: out = bf16(sum_{s=0}^{S-1} part[s]).
 // Four outputs per thread; n % 4 tails handled one by one.
 __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restrict__ part,
@@ -1073,6 +1376,24 @@ hipError_t launch_pp(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipSt
   return hipGetLastError();
 }
 
+template <bool NESTED, bool GROUPED>
+hipError_t launch_rb(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
+  auto kern = k_rb<NESTED, GROUPED>;
+  static const bool attr_done = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, RB::kLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)attr_done;
+  GemmParams q = p;
+  q.m_tiles = static_cast<int32_t>(m_tiles);
+  const int64_t tiles = ((n_cols + RB::BN - 1) / RB::BN) * m_tiles * p.splits;
+  if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kern<<<dim3(static_cast<unsigned>(tiles)), RB::kThreads, RB::kLds, stream>>>(q);
+  return hipGetLastError();
+}
+
 template <bool TRANS, bool GROUPED>
 hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_tiles,
                          int64_t n_cols, hipStream_t stream) {
@@ -1085,6 +1406,12 @@ hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_t
   if (bm == 256 && bn == 256 && c == 0) {
     return nested ? launch_pp<TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
                   : launch_pp<TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
+  }
+  if constexpr (!TRANS) {
+    if (bm == 256 && bn == 256 && c == 3) {
+      return nested ? launch_rb<true, GROUPED>(p, m_tiles, n_cols, stream)
+                    : launch_rb<false, GROUPED>(p, m_tiles, n_cols, stream);
+    }
   }
   NF4_CASE(256, 256, 2)
   NF4_CASE(128, 256, 1)
@@ -1148,9 +1475,11 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   if (o_bm == 64 || o_bm == 128 || o_bm == 256) pl.bm = o_bm;
   if (o_bn == 128 || o_bn == 256) pl.bn = o_bn;
   if (pl.bm == 256) pl.bn = 256;                   // 256 x 128 at BK 128 exceeds the LDS
-  // 256 x 256 runs the ping-pong kernel (consumers = 0); NF4_CONSUMERS=2
-  // selects the producer/consumer kernel with 8 MFMA waves instead
-  pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : 0) : 1;
+  // 256 x 256: the forward runs the register-operand kernel (consumers = 3),
+  // the input gradient the ping-pong kernel (consumers = 0); NF4_CONSUMERS=2
+  // selects the producer/consumer kernel with 8 MFMA waves, NF4_CONSUMERS=4
+  // the ping-pong kernel for the forward too
+  pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
   if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
   const int bk = 16384 / pl.bn;
   const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + pl.bn - 1) / pl.bn);

@@ -16,8 +16,11 @@ from gpu_util import DEV, abs_bits, assert_close, bits_of, ref_bits, upload
 
 pytestmark = pytest.mark.gpu
 
-# (rows, columns, MFMA waves per SIMD beside the expanding wave; 0 = ping-pong)
-TILES = [(256, 256, 0), (256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1), (128, 128, 1), (64, 128, 1)]
+# (rows, columns, kernel choice).  256 x 256: 0 = default (register-operand
+# forward, ping-pong input gradient), 4 = ping-pong for both, 2 = producer /
+# consumer kernel.  Smaller tiles: MFMA waves per SIMD beside the expanding wave.
+TILES = [(256, 256, 0), (256, 256, 4), (256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1),
+         (128, 128, 1), (64, 128, 1)]
 
 
 @pytest.fixture
@@ -66,3 +69,22 @@ def test_tile_vs_oracle(M, N, K, bm, bn, consumers, splits, plan_override):
     assert_close(y, O.matmul_fwd(xb, wb), "y", O.matmul_fwd(abs_bits(xb), aw), K)
     gx = api.nf4_matmul_bwd_input(gy.to(DEV), wq)
     assert_close(gx, O.matmul_bwd_input(gyb, wb), "grad_x", O.matmul_bwd_input(abs_bits(gyb), aw), N)
+
+
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 448])
+def test_register_operand_forward_step_counts(K, nested, plan_override):
+    """The register-operand forward runs its steps three at a time: 1, 2, 3,
+    4, 5 and 7 steps per workgroup, ragged rows and columns, against the oracle."""
+    plan_override(256, 256, 0, 1)
+    M, N = 300, 264
+    w = WL.weight_f32(N, K, WL.W_TINY, 700 + K)
+    ref = O.quantize_nf4(w, nested=nested)
+    wq = upload(ref, N, K, nested)
+    wb = ref_bits(ref, (N, K))
+    x = WL.x_bf16(M, K, WL.W_TINY, 701 + K)
+    xb = WL.bf16_bits(x)
+    y = api.nf4_matmul_fwd(x.to(DEV), wq)
+    assert_close(y, O.matmul_fwd(xb, wb), f"y K={K}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+    y2 = api.nf4_matmul_fwd(x.to(DEV), wq)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
