@@ -1243,6 +1243,9 @@ __global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
       wait_vm(ic<2 * kCopies>{});                  // weights of step i+1 landed (batch i-2 done)
       asm volatile("" ::: "memory");
       const Staged r = read_unit(ic<(P + 1) % 3>{});
+      // the nested-scale lookup waits on LDS: do it before the slice-1
+      // fragment reads are in flight
+      const float a_next = unit_scale(r);
       Lut lt;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -1251,9 +1254,9 @@ __global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
         if (kk + 1 < 4) load_a(P, kk + 1, fn);
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi)
-          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc[mi], bw[kk], acc[mi], 0, 0, 0);
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[kk], fc[mi], acc[mi], 0, 0, 0);
         if (kk == 0) {
-          lt = make_lut(code, unit_scale(r));
+          lt = make_lut(code, a_next);
         } else {
           uint32_t o[4];
           expand8(r.pk[kk - 1], lt, o);
@@ -1293,18 +1296,39 @@ __global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
   }
 
   // ---- epilogue -----------------------------------------------------------------------
-  const int64_t col = col0 + 32 * wave + r32;
-  if (col < N) {
+  // The MFMAs take the weights as the first operand, so accumulator mi holds
+  // the transposed 32 x 32 block: lane l has output row 32mi + l%32 and, for
+  // register v, column 32w + 8(v/4) + 4h + v%4 -- four consecutive columns
+  // per register group, stored as one 8-byte (bf16) or 16-byte (fp32) write.
+  const int64_t ncol0 = col0 + 32 * wave + 4 * h;
+  const bool vec_ok = (N & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.splits == 1 ? static_cast<void*>(p.C)
+                                                                 : static_cast<void*>(p.partial)) &
+                       15) == 0;
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi) {
+  for (int mi = 0; mi < 8; ++mi) {
+    const int64_t row = row0 + 32 * mi + r32;
+    if (row >= row_end) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + 32 * mi + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row >= row_end) continue;
-        if (p.splits == 1) {
-          p.C[row * N + col] = to_bf16(acc[mi][v]);
+    for (int g = 0; g < 4; ++g) {
+      const int64_t col = ncol0 + 8 * g;
+      if (col >= N) continue;
+      const float v0 = acc[mi][4 * g], v1 = acc[mi][4 * g + 1], v2 = acc[mi][4 * g + 2], v3 = acc[mi][4 * g + 3];
+      if (p.splits == 1) {
+        uint16_t* dst = p.C + row * N + col;
+        if (vec_ok && col + 3 < N) {
+          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         } else {
-          p.partial[(static_cast<int64_t>(z) * p.M + row) * N + col] = acc[mi][v];
+          const float vv[4] = {v0, v1, v2, v3};
+          for (int c = 0; c < 4 && col + c < N; ++c) dst[c] = to_bf16(vv[c]);
+        }
+      } else {
+        float* dst = p.partial + (static_cast<int64_t>(z) * p.M + row) * N + col;
+        if (vec_ok && col + 3 < N) {
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v0, v1, v2, v3};
+        } else {
+          const float vv[4] = {v0, v1, v2, v3};
+          for (int c = 0; c < 4 && col + c < N; ++c) dst[c] = vv[c];
         }
       }
     }
