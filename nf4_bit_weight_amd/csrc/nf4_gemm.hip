@@ -1024,23 +1024,27 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
 // One barrier per step: every wave's activation copy of step i has landed
 // (own vmcnt, then the barrier) and every wave has finished reading the
 // stage that the step's new copy overwrites.
+template <int WAVES>
 struct RB {
-  static constexpr int BM = 256, BN = 256, BK = 64;
-  static constexpr int kThreads = 512;
+  static constexpr int BM = 256, BN = 32 * WAVES, BK = 64;
+  static constexpr int kThreads = 64 * WAVES;
   static constexpr int kStages = 3;
   static constexpr int kAElems = BM * BK;              // bf16 per activation stage (32 KB)
+  static constexpr int kARows = BM / WAVES;            // activation rows each wave copies
   static constexpr int kWWave = 1536;                  // per wave: 1 KB packed, 256 B scale, 256 B nested
-  static constexpr int kWSlot = 8 * kWWave;            // 12 KB
+  static constexpr int kWSlot = WAVES * kWWave;
   static constexpr int kWOff = kStages * kAElems * 2;  // 96 KB
   static constexpr int kLds = kWOff + kStages * kWSlot;
 };
-static_assert(RB::kLds + 1024 <= 160 * 1024, "LDS budget of one workgroup");
+static_assert(RB<8>::kLds + 1024 <= 160 * 1024, "LDS budget of one workgroup");
 
-template <bool NESTED, bool GROUPED>
-__global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
-  constexpr int BM = RB::BM, BN = RB::BN, BK = RB::BK;
-  // per-wave copy instructions of one step: 4 activation, packed, scale (+ nested)
-  constexpr int kCopies = NESTED ? 7 : 6;
+template <int WAVES, bool NESTED, bool GROUPED>
+__global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
+  using R = RB<WAVES>;
+  constexpr int BM = R::BM, BN = R::BN, BK = R::BK;
+  constexpr int kAJ = R::kARows / 8;               // activation copy instructions per wave
+  // per-wave copy instructions of one step: activation, packed, scale (+ nested)
+  constexpr int kCopies = kAJ + (NESTED ? 3 : 2);
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ float sncode[256];
 
@@ -1086,29 +1090,29 @@ __global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
   for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
   const float off = NESTED ? p.w.nested_offset[0] : 0.f;
 
-  // ---- activation copies: wave w copies rows 32w .. 32w+31, 8 rows per
-  // instruction, 16-byte units swizzled (swz) as the fragment reads expect
+  // ---- activation copies: wave w copies rows kARows*w .. +kARows-1, 8 rows
+  // per instruction, 16-byte units swizzled (swz) as the fragment reads expect
   const int a_r_in = lane >> 3, a_unit = lane & 7;
-  const uint16_t* a_row_ptr[4];
-  int a_colofs[4];
+  const uint16_t* a_row_ptr[kAJ];
+  int a_colofs[kAJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 32 * wave + 8 * j + a_r_in;
+  for (int j = 0; j < kAJ; ++j) {
+    const int r = R::kARows * wave + 8 * j + a_r_in;
     int64_t row = row0 + r;
     row = row < row_end ? row : row_end - 1;
     a_row_ptr[j] = p.A + row * K;
     a_colofs[j] = 8 * swz(r, a_unit);
   }
-  auto stage_ptr = [&](int stage) { return lds + stage * RB::kAElems; };
+  auto stage_ptr = [&](int stage) { return lds + stage * R::kAElems; };
   auto issue_a = [&](int i, int stage) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
     const int64_t c0 = static_cast<int64_t>(kt) * BK;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kAJ; ++j) {
       int64_t col = c0 + a_colofs[j];
       col = col < K ? col : K - 8;
       const uint16_t* src = a_row_ptr[j] + col;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_ptr(stage) + (32 * wave + 8 * j) * BK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_ptr(stage) + (R::kARows * wave + 8 * j) * BK), 16, 0, 0);
     }
   };
 
@@ -1121,10 +1125,10 @@ __global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
   const int64_t wrow_g = wrow_base + wrow;
   const uint8_t* const pk_base = p.w.packed + ((wrow_g * K) >> 1) + 16 * h;
   const int64_t blocks_per_row = K / BK;
-  char* const w_area = reinterpret_cast<char*>(lds) + RB::kWOff;
+  char* const w_area = reinterpret_cast<char*>(lds) + R::kWOff;
   auto issue_w = [&](int i, int slot) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
-    char* sl = w_area + slot * RB::kWSlot + wave * RB::kWWave;
+    char* sl = w_area + slot * R::kWSlot + wave * R::kWWave;
     const uint8_t* src = row_ok ? pk_base + static_cast<int64_t>(kt) * (BK / 2) : p.w.packed;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)sl, 16, 0, 0);
     const int64_t b = row_ok ? wrow_g * blocks_per_row + kt : 0;
@@ -1139,33 +1143,28 @@ __global__ __launch_bounds__(512, 1) void k_rb(GemmParams p) {
     }
   };
   const uint32_t st_pk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) +
-                         wave * RB::kWWave + 16 * lane;
+                         wave * R::kWWave + 16 * lane;
   const uint32_t st_sc = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) +
-                         wave * RB::kWWave + 1024 + 4 * lane;
+                         wave * R::kWWave + 1024 + 4 * lane;
   const uint32_t st_ncode = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)sncode));
   struct Staged {
     u32x4_t pk;
     uint32_t sc, s2;
   };
-#define NF4_RB_READ(OFF)                                                                   \
-  asm volatile("ds_read_b128 %0, %3 offset:" #OFF "\n\t"                                   \
-               "ds_read_b32 %1, %4 offset:" #OFF "\n\t"                                    \
-               "ds_read_b32 %2, %4 offset:" #OFF "+256\n\t"                                \
-               "s_waitcnt lgkmcnt(0)"                                                      \
-               : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)                                        \
-               : "v"(st_pk), "v"(st_sc)                                                    \
-               : "memory")
   auto read_unit = [&](auto slot_c) __attribute__((always_inline)) {
-    constexpr int slot = decltype(slot_c)::value;
-    static_assert(RB::kWSlot == 12288, "slot offsets below");
+    constexpr int off = decltype(slot_c)::value * R::kWSlot;
+    static_assert(2 * R::kWSlot + 256 < 65536, "slot offsets fit the ds immediate");
     Staged r;
-    if constexpr (slot == 0) NF4_RB_READ(0);
-    else if constexpr (slot == 1) NF4_RB_READ(12288);
-    else NF4_RB_READ(24576);
+    asm volatile("ds_read_b128 %0, %3 offset:%5\n\t"
+                 "ds_read_b32 %1, %4 offset:%5\n\t"
+                 "ds_read_b32 %2, %4 offset:%6\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)
+                 : "v"(st_pk), "v"(st_sc), "i"(off), "i"(off + 256)
+                 : "memory");
     if constexpr (!NESTED) r.s2 = 0;
     return r;
   };
-#undef NF4_RB_READ
   auto unit_scale = [&](const Staged& r) __attribute__((always_inline)) {
     float a;
     if constexpr (NESTED) {
@@ -1400,21 +1399,22 @@ hipError_t launch_pp(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipSt
   return hipGetLastError();
 }
 
-template <bool NESTED, bool GROUPED>
+template <int WAVES, bool NESTED, bool GROUPED>
 hipError_t launch_rb(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
-  auto kern = k_rb<NESTED, GROUPED>;
+  using R = RB<WAVES>;
+  auto kern = k_rb<WAVES, NESTED, GROUPED>;
   static const bool attr_done = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, RB::kLds);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, R::kLds);
     (void)hipGetLastError();
     return true;
   }();
   (void)attr_done;
   GemmParams q = p;
   q.m_tiles = static_cast<int32_t>(m_tiles);
-  const int64_t tiles = ((n_cols + RB::BN - 1) / RB::BN) * m_tiles * p.splits;
+  const int64_t tiles = ((n_cols + R::BN - 1) / R::BN) * m_tiles * p.splits;
   if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  kern<<<dim3(static_cast<unsigned>(tiles)), RB::kThreads, RB::kLds, stream>>>(q);
+  kern<<<dim3(static_cast<unsigned>(tiles)), R::kThreads, R::kLds, stream>>>(q);
   return hipGetLastError();
 }
 
@@ -1433,8 +1433,12 @@ hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_t
   }
   if constexpr (!TRANS) {
     if (bm == 256 && bn == 256 && c == 3) {
-      return nested ? launch_rb<true, GROUPED>(p, m_tiles, n_cols, stream)
-                    : launch_rb<false, GROUPED>(p, m_tiles, n_cols, stream);
+      return nested ? launch_rb<8, true, GROUPED>(p, m_tiles, n_cols, stream)
+                    : launch_rb<8, false, GROUPED>(p, m_tiles, n_cols, stream);
+    }
+    if (bm == 256 && bn == 128 && c == 3) {
+      return nested ? launch_rb<4, true, GROUPED>(p, m_tiles, n_cols, stream)
+                    : launch_rb<4, false, GROUPED>(p, m_tiles, n_cols, stream);
     }
   }
   NF4_CASE(256, 256, 2)
@@ -1485,7 +1489,9 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // M = 2048): large products take 256 x 256 (each expanded weight serves 256
   // rows), mid-size ones 128 x 128 (4x the tiles), small ones 64 x 128.
   const double macs = static_cast<double>(M) * static_cast<double>(nc) * static_cast<double>(kc);
-  if (macs >= 2e10 && M > 128) {
+  // The forward takes the register-operand kernel from 4e9 MACs at M > 128
+  // (tile width and split chosen by the cost model below).
+  if ((macs >= 2e10 || (kind == GemmKind::kFwd && macs >= 4e9)) && M > 128) {
     pl.bm = 256; pl.bn = 256;
   } else if (macs >= 4e9 && M > 64) {
     pl.bm = 128; pl.bn = 128;
@@ -1498,14 +1504,15 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   const int o_c = env_int("NF4_CONSUMERS");
   if (o_bm == 64 || o_bm == 128 || o_bm == 256) pl.bm = o_bm;
   if (o_bn == 128 || o_bn == 256) pl.bn = o_bn;
-  if (pl.bm == 256) pl.bn = 256;                   // 256 x 128 at BK 128 exceeds the LDS
+  // 256 x 128 exists only as the register-operand forward (NF4_BN=128)
+  if (pl.bm == 256 && !(kind == GemmKind::kFwd && o_bn == 128 && o_c != 2 && o_c != 4)) pl.bn = 256;
   // 256 x 256: the forward runs the register-operand kernel (consumers = 3),
   // the input gradient the ping-pong kernel (consumers = 0); NF4_CONSUMERS=2
   // selects the producer/consumer kernel with 8 MFMA waves, NF4_CONSUMERS=4
   // the ping-pong kernel for the forward too
   pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
   if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
-  const int bk = 16384 / pl.bn;
+  const int bk = (pl.consumers == 3) ? 64 : 16384 / pl.bn;
   const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + pl.bn - 1) / pl.bn);
   const int64_t ksteps = (kc + bk - 1) / bk;
   // Split count: minimise (rounds of workgroups over the compute units) x
@@ -1513,16 +1520,45 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // moves (4 S + 2) M Nc bytes.  Step time is modelled at ~3.8 TFLOP/s per
   // compute unit and the reduction at ~5 TB/s; each split keeps >= 8 steps.
   int s = 1;
+  // Split count (and, for the register-operand forward, the tile width):
+  // minimise rounds of workgroups over the compute units x (steps per
+  // workgroup x step time + ~4 us of prologue and epilogue) + the split
+  // traffic (the partials written and read back and the bf16 result).  Step
+  // times measured on MI355X: 256 x 256 register-operand ~1.75 us, 256 x 128
+  // ~1.25 us; the other kernels are modelled at ~3.8 TFLOP/s per compute
+  // unit.  Each split keeps >= 8 steps.
   {
-    const double t_step = 2.0 * pl.bm * pl.bn * bk / 3.8e6;                  // us
+    const bool rb = pl.consumers == 3;
+    // measured per kernel family: the register-operand forward's split
+    // traffic is charged at (8 S + 2) M Nc bytes / 2.5 TB/s, the other
+    // kernels' at (4 S + 2) M Nc bytes / 5 TB/s
+    auto split_cost = [&](int c) {
+      const double mn = static_cast<double>(M) * static_cast<double>(nc);
+      return rb ? (8.0 * c + 2.0) * mn / 2.5e6 : (4.0 * c + 2.0) * mn / 5.0e6;
+    };
+    auto cost = [&](int bn_c, int bk_c, double t_step, int c) {
+      const int64_t tl = ((M + pl.bm - 1) / pl.bm) * ((nc + bn_c - 1) / bn_c);
+      const int64_t ks = (kc + bk_c - 1) / bk_c;
+      const int64_t rounds = (tl * c + cus - 1) / cus;
+      const int64_t steps = (ks + c - 1) / c;
+      double t = static_cast<double>(rounds) * (static_cast<double>(steps) * t_step + 4.0);
+      if (c > 1) t += split_cost(c);
+      return t;
+    };
+    const double t_step = rb ? (pl.bn == 256 ? 1.75 : 1.25) : 2.0 * pl.bm * pl.bn * bk / 3.8e6;
     double best = 0;
     for (int c = 1; c <= 8; ++c) {
       if (c > 1 && ksteps < 8 * c) break;
-      const int64_t rounds = (tiles * c + cus - 1) / cus;
-      const int64_t steps = (ksteps + c - 1) / c;
-      double t = static_cast<double>(rounds) * static_cast<double>(steps) * t_step;
-      if (c > 1) t += (4.0 * c + 2.0) * static_cast<double>(M) * static_cast<double>(nc) / 5.0e6;
+      const double t = cost(pl.bn, bk, t_step, c);
       if (c == 1 || t < best) { best = t; s = c; }
+    }
+    // the 4-wave 256 x 128 register-operand forward, unless a width was forced
+    if (rb && pl.bn == 256 && o_bn == 0) {
+      for (int c = 1; c <= 8; ++c) {
+        if (c > 1 && ksteps < 8 * c) break;
+        const double t = cost(128, 64, 1.25, c);
+        if (t < best) { best = t; s = c; pl.bn = 128; }
+      }
     }
   }
   if (o_s >= 1 && o_s <= 16) s = o_s;

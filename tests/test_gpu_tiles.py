@@ -18,9 +18,11 @@ pytestmark = pytest.mark.gpu
 
 # (rows, columns, kernel choice).  256 x 256: 0 = default (register-operand
 # forward, ping-pong input gradient), 4 = ping-pong for both, 2 = producer /
-# consumer kernel.  Smaller tiles: MFMA waves per SIMD beside the expanding wave.
-TILES = [(256, 256, 0), (256, 256, 4), (256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1),
-         (128, 128, 1), (64, 128, 1)]
+# consumer kernel; 256 x 128 is the 4-wave register-operand forward (the input
+# gradient falls back to 256 x 256).  Smaller tiles: MFMA waves per SIMD beside
+# the expanding wave.
+TILES = [(256, 256, 0), (256, 128, 0), (256, 256, 4), (256, 256, 2), (128, 256, 1), (128, 256, 2),
+         (64, 256, 1), (128, 128, 1), (64, 128, 1)]
 
 
 @pytest.fixture
@@ -71,12 +73,13 @@ def test_tile_vs_oracle(M, N, K, bm, bn, consumers, splits, plan_override):
     assert_close(gx, O.matmul_bwd_input(gyb, wb), "grad_x", O.matmul_bwd_input(abs_bits(gyb), aw), N)
 
 
+@pytest.mark.parametrize("bn", [256, 128])
 @pytest.mark.parametrize("nested", [False, True])
 @pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 448])
-def test_register_operand_forward_step_counts(K, nested, plan_override):
+def test_register_operand_forward_step_counts(K, nested, bn, plan_override):
     """The register-operand forward runs its steps three at a time: 1, 2, 3,
     4, 5 and 7 steps per workgroup, ragged rows and columns, against the oracle."""
-    plan_override(256, 256, 0, 1)
+    plan_override(256, bn, 0, 1)
     M, N = 300, 264
     w = WL.weight_f32(N, K, WL.W_TINY, 700 + K)
     ref = O.quantize_nf4(w, nested=nested)
