@@ -863,9 +863,11 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       }
     }
   };
+  // slice 0 of a step's fragments is read ahead, right after the barrier
+  // that ends the previous step (fpre)
+  Frags fpre;
   auto compute = [&](int stage, int buf, bool with_dma) __attribute__((always_inline)) {
-    Frags f0, f1;
-    load_frags(stage, buf, 0, f0);
+    Frags f0 = fpre, f1;
 #pragma unroll
     for (int kk = 0; kk < PP::KK; ++kk) {
       Frags& fc = (kk & 1) ? f1 : f0;
@@ -875,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       for (int i = 0; i < PP::MI; ++i)
 #pragma unroll
         for (int j = 0; j < PP::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.b[j], fc.a[i], acc[i][j], 0, 0, 0);
       if (with_dma) dma(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -911,7 +913,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       for (int ii = 0; ii < PP::MI; ++ii)
 #pragma unroll
         for (int j = 0; j < PP::NI; ++j)
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[ii], fc.b[j], acc[ii][j], 0, 0, 0);
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.b[j], fc.a[ii], acc[ii][j], 0, 0, 0);
       if (kk == 0) {
         lt = make_lut(code, valid ? a : 0.f);
       } else {
@@ -962,6 +964,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     __syncthreads();                               // every wave's copies of steps 0 and 1 landed
     expand(0, 0, 0, false);
     __syncthreads();
+    if constexpr (TRANS) load_frags(0, 0, 0, fpre);
     auto step = [&](int i, auto ph) __attribute__((always_inline)) {
       constexpr int P = decltype(ph)::value;
       ci = i;
@@ -978,6 +981,8 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
         if (mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, false);
       }
       end_step();
+      // slice 0 of step i+1 (a harmless re-read of landed data after the last step)
+      if constexpr (TRANS) load_frags((P + 1) & 1, (P + 1) & 1, 0, fpre);
     };
     int i = 0;
     for (; i + 2 <= n; i += 2) {
@@ -988,20 +993,43 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   }
 
   // ---- epilogue -------------------------------------------------------------------
+  // The MFMAs take the weight fragments as the first operand, so acc[i][j]
+  // is the transposed 32 x 32 block: lane l holds output row
+  // wm*WM + 32i + l%32 and, in register v, column wn*WN + 32j + 8(v/4) + 4h +
+  // v%4 -- four consecutive columns per register group, one 8-byte (bf16) or
+  // 16-byte (fp32) store each.
+  const bool vec_ok = (Nc & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(p.splits == 1 ? static_cast<void*>(p.C)
+                                                                 : static_cast<void*>(p.partial)) &
+                       15) == 0;
 #pragma unroll
   for (int i = 0; i < PP::MI; ++i) {
+    const int64_t row = row0 + wm * PP::WM + 32 * i + r32;
+    if (row >= row_end) continue;
 #pragma unroll
     for (int j = 0; j < PP::NI; ++j) {
-      const int64_t col = col0 + wn * PP::WN + 32 * j + r32;
-      if (col >= Nc) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + wm * PP::WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row >= row_end) continue;
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = col0 + wn * PP::WN + 32 * j + 8 * g + 4 * h;
+        if (col >= Nc) continue;
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
         if (p.splits == 1) {
-          p.C[row * Nc + col] = to_bf16(acc[i][j][v]);
+          uint16_t* dst = p.C + row * Nc + col;
+          if (vec_ok && col + 3 < Nc) {
+            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+            for (int c = 0; c < 4 && col + c < Nc; ++c) dst[c] = to_bf16(vv[c]);
+          }
         } else {
-          p.partial[(static_cast<int64_t>(z) * p.M + row) * Nc + col] = acc[i][j][v];
+          float* dst = p.partial + (static_cast<int64_t>(z) * p.M + row) * Nc + col;
+          if (vec_ok && col + 3 < Nc) {
+            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v0, v1, v2, v3};
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+            for (int c = 0; c < 4 && col + c < Nc; ++c) dst[c] = vv[c];
+          }
         }
       }
     }
