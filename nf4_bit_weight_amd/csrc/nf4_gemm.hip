@@ -877,7 +877,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       for (int i = 0; i < PP::MI; ++i)
 #pragma unroll
         for (int j = 0; j < PP::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.b[j], fc.a[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
       if (with_dma) dma(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -913,7 +913,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       for (int ii = 0; ii < PP::MI; ++ii)
 #pragma unroll
         for (int j = 0; j < PP::NI; ++j)
-          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.b[j], fc.a[ii], acc[ii][j], 0, 0, 0);
+          acc[ii][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[ii], fc.b[j], acc[ii][j], 0, 0, 0);
       if (kk == 0) {
         lt = make_lut(code, valid ? a : 0.f);
       } else {
@@ -993,43 +993,20 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   }
 
   // ---- epilogue -------------------------------------------------------------------
-  // The MFMAs take the weight fragments as the first operand, so acc[i][j]
-  // is the transposed 32 x 32 block: lane l holds output row
-  // wm*WM + 32i + l%32 and, in register v, column wn*WN + 32j + 8(v/4) + 4h +
-  // v%4 -- four consecutive columns per register group, one 8-byte (bf16) or
-  // 16-byte (fp32) store each.
-  const bool vec_ok = (Nc & 3) == 0 &&
-                      (reinterpret_cast<uintptr_t>(p.splits == 1 ? static_cast<void*>(p.C)
-                                                                 : static_cast<void*>(p.partial)) &
-                       15) == 0;
 #pragma unroll
   for (int i = 0; i < PP::MI; ++i) {
-    const int64_t row = row0 + wm * PP::WM + 32 * i + r32;
-    if (row >= row_end) continue;
 #pragma unroll
     for (int j = 0; j < PP::NI; ++j) {
+      const int64_t col = col0 + wn * PP::WN + 32 * j + r32;
+      if (col >= Nc) continue;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t col = col0 + wn * PP::WN + 32 * j + 8 * g + 4 * h;
-        if (col >= Nc) continue;
-        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + wm * PP::WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row >= row_end) continue;
         if (p.splits == 1) {
-          uint16_t* dst = p.C + row * Nc + col;
-          if (vec_ok && col + 3 < Nc) {
-            *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
-            for (int c = 0; c < 4 && col + c < Nc; ++c) dst[c] = to_bf16(vv[c]);
-          }
+          p.C[row * Nc + col] = to_bf16(acc[i][j][v]);
         } else {
-          float* dst = p.partial + (static_cast<int64_t>(z) * p.M + row) * Nc + col;
-          if (vec_ok && col + 3 < Nc) {
-            *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{v0, v1, v2, v3};
-          } else {
-            const float vv[4] = {v0, v1, v2, v3};
-            for (int c = 0; c < 4 && col + c < Nc; ++c) dst[c] = vv[c];
-          }
+          p.partial[(static_cast<int64_t>(z) * p.M + row) * Nc + col] = acc[i][j][v];
         }
       }
     }
@@ -1072,7 +1049,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
   constexpr int BM = R::BM, BN = R::BN, BK = R::BK;
   constexpr int kAJ = R::kARows / 8;               // activation copy instructions per wave
   // per-wave copy instructions of one step: activation, packed, scale (+ nested)
-  constexpr int kCopies = kAJ + (NESTED ? 3 : 2);
+  constexpr int kWCopies = NESTED ? 3 : 2;          // packed, scale (+ nested)
+  constexpr int kCopies = kAJ + kWCopies;
+  static_assert(2 * kCopies <= 63, "outstanding copies fit the vmcnt field");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ float sncode[256];
 
@@ -1258,7 +1237,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
     // MFMAs are issued the wave waits for its part of A(i+1), joins the
     // barrier and reads slice 0 of step i+1 while those MFMAs still run.
     bf16x8_t f0[8], f1[8];
-    wait_vm(ic<2 * kCopies - 4>{});                // own part of A(0) landed
+    wait_vm(ic<kAJ + 2 * kWCopies>{});             // own part of A(0) landed (W(1), A(1), W(2) may fly)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     load_a(0, 0, f0);
@@ -1305,7 +1284,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
       asm volatile("" ::: "memory");
       // A(i+1) was the first part of batch i-1: W(i+2) of that batch and all
       // of batch i may still be in flight
-      wait_vm(ic<kCopies + kCopies - 4>{});
+      wait_vm(ic<kCopies + kWCopies>{});
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);

@@ -91,3 +91,27 @@ def test_register_operand_forward_step_counts(K, nested, bn, plan_override):
     assert_close(y, O.matmul_fwd(xb, wb), f"y K={K}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
     y2 = api.nf4_matmul_fwd(x.to(DEV), wq)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("bn", [128, 256])
+def test_register_operand_forward_repeats_bitwise(bn, plan_override):
+    """Regression: each copy wait of the register-operand forward must cover
+    the whole activation copy of its step for both wave counts (a short wait
+    let a step read a half-landed stage).  Many steps per workgroup, several
+    launches, every output bitwise equal, sampled columns against the oracle."""
+    plan_override(256, bn, 0, 1)
+    M, N, K = 256, 1024, 4096
+    w = WL.weight_f32(N, K, WL.W_TINY, 900 + bn)
+    ref = O.quantize_nf4(w, nested=True)
+    wq = upload(ref, N, K, True)
+    x = WL.x_bf16(M, K, WL.W_TINY, 901)
+    xd = x.to(DEV)
+    y0 = api.nf4_matmul_fwd(xd, wq).clone()
+    for _ in range(8):
+        y = api.nf4_matmul_fwd(xd, wq)
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), "not bitwise repeatable"
+    cols = np.sort(np.random.default_rng(bn).choice(N, size=48, replace=False))
+    wb = ref_bits(ref, (N, K))[cols]
+    xb = WL.bf16_bits(x)
+    assert_close(y0[:, torch.from_numpy(cols).to(DEV)], O.matmul_fwd(xb, wb), "sampled",
+                 O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
