@@ -1,26 +1,35 @@
 // Small-M forward y = x . W_hat^T (M <= 32): weight-streaming kernel.
 //
-// At decode sizes the product is bound by HBM: every packed byte of W is used
-// by at most 32 rows of x (Soup issue #842, "Nuance", on the small-batch regime
-// where a fused 4-bit GEMV is the fast path).  The kernel therefore streams W
-// once, with each lane expanding whole 64-blocks, and keeps x on chip.
+// At decode sizes the product is bound by HBM and by the expansion: every
+// packed byte of W is used by at most 32 rows of x (Soup issue #842, "Nuance",
+// on the small-batch regime where a fused 4-bit GEMV is the fast path).  The
+// kernel therefore streams W once, with each lane expanding whole 64-blocks,
+// and keeps x on chip.
 //
-//   * A wave owns MP rows of W (MP = 16 for M <= 16, 32 otherwise) and one
-//     contraction chunk.  The MFMA is v_mfma_f32_16x16x32_bf16 (MP = 16) or
-//     v_mfma_f32_32x32x16_bf16 (MP = 32); its A operand is x (rows >= M are
-//     zero), its B operand the expanded weights.
+//   * A workgroup owns RW * MP rows of W and one contraction chunk.  Its
+//     RW * KW waves are arranged as RW row groups of MP rows times KW
+//     contraction slices: the KW waves of a row group split the chunk's steps
+//     between them, and their fp32 results are added through LDS in the fixed
+//     order 0 .. KW-1.  Splitting the contraction inside the workgroup gives
+//     enough waves to cover HBM latency without partial sums in HBM; chunks
+//     across workgroups (summed by the fixed-order split reduction) are only
+//     used when the x chunk would not fit in LDS.
+//   * The MFMA is v_mfma_f32_16x16x32_bf16 (MP = 16) or
+//     v_mfma_f32_32x32x16_bf16 (MP = 32); its A operand is x (rows >= M read
+//     a zero row), its B operand the expanded weights.
 //   * The contraction is permuted inside each step so that a lane's k-group
 //     is one whole NF4 block: lane (n = l % MP, g = l / MP) of MFMA t reads
-//     k = 64 * (G * s + g) + 8 t .. + 7 of step s (G = 64 / MP groups).  A
+//     k = 64 * (G * s + g) + 8 t .. + 7 of step s (G = 64 / MP blocks).  A
 //     lane thus loads its block's 32 packed bytes with two 16-byte loads (the
 //     G lanes of one row read G consecutive blocks: whole 128-byte lines),
 //     builds one 16-entry byte table per block and expands one dword per MFMA.
 //   * Within each 8-element group the expansion emits the order
 //     (0, 2, 4, 6, 1, 3, 5, 7), which saves the final interleave; x is staged
 //     into LDS in the same order, so every product pairs the right elements.
-//   * Packed loads run PD steps ahead in registers.  The contraction is split
-//     into chunks so that enough workgroups exist; chunk partials (fp32) are
-//     added by the fixed-order split-K reduction, as in the tiled kernel.
+//   * Packed loads run PD steps ahead in registers, and the first PD are in
+//     flight while x is staged.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "nf4_device.hpp"
@@ -29,8 +38,9 @@
 namespace nf4 {
 namespace {
 
-constexpr int kGemvThreads = 256;   // 4 waves
-constexpr int kPD = 4;              // packed-weight prefetch distance (steps)
+constexpr int kPD = 4;                    // packed-weight prefetch distance (steps)
+constexpr int kXBudgetBytes = 64 * 1024;  // LDS for the staged x chunk (M + 1 rows)
+constexpr int kMaxWaves = 16;
 
 struct GemvParams {
   const uint16_t* x;     // [M, K] bf16
@@ -46,8 +56,6 @@ template <int MP>
 struct Gv {
   static constexpr int G = 64 / MP;               // blocks per step
   static constexpr int kStepK = 64 * G;           // 256 or 128
-  static constexpr int kRowsWG = 4 * MP;          // W rows per workgroup
-  static constexpr int kMaxKC = MP == 16 ? 2048 : 1024;
   static constexpr int kAccRegs = MP == 16 ? 4 : 16;
 };
 
@@ -72,14 +80,17 @@ __device__ __forceinline__ void expand8_eo(uint32_t p, const Lut& t, uint32_t (&
   out[3] = perm(ho, lo, 0x07030602u);
 }
 
-template <int MP, bool NESTED>
-__global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvParams p) {
+template <int MP, int RW, int KW, bool NESTED>
+__global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   using S = Gv<MP>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [MP][kc + 8]
+  constexpr int kThr = 64 * RW * KW;
+  // [M + 1][kc + 8] bf16 (row M is zero), reused for the cross-wave sums
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ float sncode[256];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rw = wave % RW, kw = wave / RW;
   const int64_t N = p.w.N, K = p.w.K;
   const int M = p.M;
   const int z = blockIdx.y;
@@ -88,32 +99,18 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvParams p) {
   const int kc = p.kc;
   const int pitch = kc + 8;                      // elements; rows land on distinct banks
 
-  if constexpr (NESTED) sncode[tid] = p.w.ncode[tid];
-
-  // ---- stage x[:, k0:k0+kc] into LDS, each 8-group as (0,2,4,6,1,3,5,7) ----
-  // rows >= M and columns >= K are zero
-  for (int c = tid; c < MP * (kc / 8); c += kGemvThreads) {
-    const int m = c / (kc / 8), c8 = c % (kc / 8);
-    const int64_t k = k0 + 8 * c8;
-    u32x4_t d = {0u, 0u, 0u, 0u};
-    if (m < M && k < K) d = *reinterpret_cast<const u32x4_t*>(p.x + static_cast<int64_t>(m) * K + k);
-    const u32x4_t o = {perm(d[1], d[0], 0x05040100u), perm(d[3], d[2], 0x05040100u),
-                       perm(d[1], d[0], 0x07060302u), perm(d[3], d[2], 0x07060302u)};
-    *reinterpret_cast<u32x4_t*>(xs + m * pitch + 8 * c8) = o;
-  }
-  __syncthreads();
-
-  float code[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
-  const float off = NESTED ? p.w.nested_offset[0] : 0.f;
+  // ---- this wave's steps of the chunk: a contiguous run ------------------------
+  const int nsteps = static_cast<int>((k1 - k0 + S::kStepK - 1) / S::kStepK);
+  const int per = (nsteps + KW - 1) / KW;
+  const int s_begin = kw * per < nsteps ? kw * per : nsteps;
+  const int s_end = s_begin + per < nsteps ? s_begin + per : nsteps;
+  const int nw = s_end - s_begin;
 
   // ---- this lane's row and block group -----------------------------------------
   const int r = lane % MP, g = lane / MP;
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * S::kRowsWG + wave * MP + r;
+  const int64_t n = (static_cast<int64_t>(blockIdx.x) * RW + rw) * MP + r;
   const bool row_ok = n < N;
   const int64_t row_base = (row_ok ? n : 0) * K;             // element offset of the row
-  const int nsteps = static_cast<int>((k1 - k0 + S::kStepK - 1) / S::kStepK);
 
   struct Raw {
     u32x4_t pk0, pk1;
@@ -121,10 +118,12 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvParams p) {
     float s2;
     bool valid;
   };
-  auto load = [&](int s, Raw& q) {
-    const int sc_ = s < nsteps ? s : nsteps - 1;
-    const int64_t koff = k0 + 64 * (S::G * sc_ + g);
-    q.valid = row_ok & (koff < k1);
+  // local step ls of this wave; past the end it reloads the last step (an
+  // address already read), so every load stays inside the tensor
+  auto load = [&](int ls, Raw& q) {
+    const int sc_ = s_begin + (ls < nw ? ls : (nw > 0 ? nw - 1 : 0));
+    const int64_t koff = k0 + static_cast<int64_t>(S::kStepK) * sc_ + 64 * g;
+    q.valid = row_ok & (koff < k1) & (nw > 0);
     const uint64_t flat = q.valid ? static_cast<uint64_t>(row_base + koff) : 0;   // multiple of 64
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + (flat >> 1));
     q.pk0 = src[0];
@@ -139,43 +138,110 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvParams p) {
     }
   };
 
-  acc_t<MP> acc;
-#pragma unroll
-  for (int i = 0; i < S::kAccRegs; ++i) acc[i] = 0.f;
-
-  // A fragment of MFMA t in step s: x row r (as the MFMA row), k-group g
-  const uint16_t* xrow = xs + r * pitch + 64 * g;
-  auto step = [&](int s, const Raw& q) {
-    float a;
-    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[q.sc], q.s2), off);
-    else a = __uint_as_float(q.sc);
-    const Lut lt = make_lut(code, q.valid ? a : 0.f);
-    const uint16_t* xa = xrow + 64 * S::G * s;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      uint32_t o[4];
-      expand8_eo(t < 4 ? q.pk0[t] : q.pk1[t - 4], lt, o);
-      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
-      const bf16x8_t afr = *reinterpret_cast<const bf16x8_t*>(xa + 8 * t);
-      if constexpr (MP == 16) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc, 0, 0, 0);
-      } else {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr, acc, 0, 0, 0);
-      }
-    }
-  };
-
   // The fences keep every prefetch where it is written: without them the
   // compiler sinks each load next to its use one iteration later.
   auto fence = [] { asm volatile("" ::: "memory"); };
+
+  // ---- prologue: every load that the first step needs is issued before the
+  // first wait, in the order it is consumed (loads complete in order) --------
+  float code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
+  const float off = NESTED ? p.w.nested_offset[0] : 0.f;
+  // the 256-entry nested table: kNC entries per thread
+  constexpr int kNC = (256 + kThr - 1) / kThr;
+  float nc_reg[kNC];
+  if constexpr (NESTED) {
+#pragma unroll
+    for (int j = 0; j < kNC; ++j) {
+      const int i = tid + j * kThr;
+      nc_reg[j] = i < 256 ? p.w.ncode[i] : 0.f;
+    }
+  }
+  // x[:, k0:k0+kc] is staged in batches of kXB 16-byte chunks per thread; each
+  // 8-group is stored as (0,2,4,6,1,3,5,7); row M and columns >= K are zero
+  constexpr int kXB = 4;
+  const int c8n = kc / 8;
+  const int nchunks = (M + 1) * c8n;
+  u32x4_t xd[kXB];
+  auto xload = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < kXB; ++j) {
+      const int c = base + tid + j * kThr;
+      xd[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (c < nchunks) {
+        const int m = c / c8n, c8 = c - m * c8n;
+        const int64_t k = k0 + 8 * c8;
+        if (m < M && k < K) xd[j] = *reinterpret_cast<const u32x4_t*>(p.x + static_cast<int64_t>(m) * K + k);
+      }
+    }
+  };
+  auto xstore = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < kXB; ++j) {
+      const int c = base + tid + j * kThr;
+      if (c < nchunks) {
+        const int m = c / c8n, c8 = c - m * c8n;
+        const u32x4_t d = xd[j];
+        const u32x4_t o = {perm(d[1], d[0], 0x05040100u), perm(d[3], d[2], 0x05040100u),
+                           perm(d[1], d[0], 0x07060302u), perm(d[3], d[2], 0x07060302u)};
+        *reinterpret_cast<u32x4_t*>(xs + m * pitch + 8 * c8) = o;
+      }
+    }
+  };
+  xload(0);
+  fence();
   Raw q0, q1, q2, q3;
   load(0, q0);
   load(1, q1);
   load(2, q2);
   load(3, q3);
   fence();
+  if constexpr (NESTED) {
+#pragma unroll
+    for (int j = 0; j < kNC; ++j) {
+      const int i = tid + j * kThr;
+      if (i < 256) sncode[i] = nc_reg[j];
+    }
+  }
+  xstore(0);
+  for (int base = kXB * kThr; base < nchunks; base += kXB * kThr) {
+    xload(base);
+    xstore(base);
+  }
+  __syncthreads();
+
+  acc_t<MP> acc;
+#pragma unroll
+  for (int i = 0; i < S::kAccRegs; ++i) acc[i] = 0.f;
+
+  // A fragment of MFMA t in step s: x row r (rows >= M read the zero row M)
+  const uint16_t* xrow = xs + (r < M ? r : M) * pitch + 64 * g;
+  auto step = [&](int ls, const Raw& q) {
+    // all eight A fragments first: their LDS latency overlaps the table build
+    const uint16_t* xa = xrow + S::kStepK * (s_begin + ls);
+    bf16x8_t afr[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) afr[t] = *reinterpret_cast<const bf16x8_t*>(xa + 8 * t);
+    float a;
+    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[q.sc], q.s2), off);
+    else a = __uint_as_float(q.sc);
+    const Lut lt = make_lut(code, q.valid ? a : 0.f);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t o[4];
+      expand8_eo(t < 4 ? q.pk0[t] : q.pk1[t - 4], lt, o);
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+      if constexpr (MP == 16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[t], bfr, acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[t], bfr, acc, 0, 0, 0);
+      }
+    }
+  };
+
   int s = 0;
-  for (; s + kPD <= nsteps; s += kPD) {
+  for (; s + kPD <= nw; s += kPD) {
     step(s, q0);
     fence();
     load(s + 4, q0);
@@ -193,9 +259,27 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvParams p) {
     load(s + 7, q3);
     fence();
   }
-  if (s < nsteps) step(s, q0);
-  if (s + 1 < nsteps) step(s + 1, q1);
-  if (s + 2 < nsteps) step(s + 2, q2);
+  if (s < nw) step(s, q0);
+  if (s + 1 < nw) step(s + 1, q1);
+  if (s + 2 < nw) step(s + 2, q2);
+
+  // ---- fixed-order sum over the KW contraction slices of each row group ------
+  if constexpr (KW > 1) {
+    __syncthreads();                                   // x is no longer read
+    float* red = reinterpret_cast<float*>(xs);         // [KW-1][RW][regs][64]
+    if (kw > 0) {
+#pragma unroll
+      for (int i = 0; i < S::kAccRegs; ++i)
+        red[(((kw - 1) * RW + rw) * S::kAccRegs + i) * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    if (kw > 0) return;
+    for (int v = 1; v < KW; ++v) {
+#pragma unroll
+      for (int i = 0; i < S::kAccRegs; ++i)
+        acc[i] = __fadd_rn(acc[i], red[(((v - 1) * RW + rw) * S::kAccRegs + i) * 64 + lane]);
+    }
+  }
 
   // ---- epilogue: lane holds output column n; rows as laid out by the MFMA ----
   if (!row_ok) return;
@@ -211,45 +295,88 @@ __global__ __launch_bounds__(kGemvThreads) void k_gemv(GemvParams p) {
   }
 }
 
-template <int MP, bool NESTED>
+// LDS of one launch: the x chunk (M + 1 rows) or the cross-wave sums, whichever is larger
+size_t gemv_lds_bytes(int mp, int rw, int kw, int64_t M, int kc) {
+  const size_t xb = static_cast<size_t>(M + 1) * static_cast<size_t>(kc + 8) * 2;
+  const size_t rb = static_cast<size_t>(kw - 1) * rw * (mp == 16 ? 4 : 16) * 64 * 4;
+  return xb > rb ? xb : rb;
+}
+
+template <int MP, int RW, int KW, bool NESTED>
 hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
-  using S = Gv<MP>;
-  auto kern = k_gemv<MP, NESTED>;
-  const size_t lds = static_cast<size_t>(MP) * (S::kMaxKC + 8) * 2;
+  auto kern = k_gemv<MP, RW, KW, NESTED>;
   static const bool attr_done = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetBytes + 4096);
     (void)hipGetLastError();
     return true;
   }();
   (void)attr_done;
-  const size_t need = static_cast<size_t>(MP) * (p.kc + 8) * 2;
-  const dim3 grid(static_cast<unsigned>((p.w.N + S::kRowsWG - 1) / S::kRowsWG),
+  const size_t need = gemv_lds_bytes(MP, RW, KW, p.M, p.kc);
+  const dim3 grid(static_cast<unsigned>((p.w.N + RW * MP - 1) / (RW * MP)),
                   static_cast<unsigned>(p.splits));
-  kern<<<grid, kGemvThreads, need, stream>>>(p);
+  kern<<<grid, 64 * RW * KW, need, stream>>>(p);
   return hipGetLastError();
 }
 
+template <int MP, int RW, bool NESTED>
+hipError_t launch_kw(int kw, const GemvParams& p, hipStream_t stream) {
+  switch (kw) {
+    case 1: return launch_gemv_t<MP, RW, 1, NESTED>(p, stream);
+    case 2: return launch_gemv_t<MP, RW, 2, NESTED>(p, stream);
+    case 4: return launch_gemv_t<MP, RW, 4, NESTED>(p, stream);
+    case 8: if constexpr (RW <= 2) return launch_gemv_t<MP, RW, 8, NESTED>(p, stream); break;
+    case 16: if constexpr (RW == 1) return launch_gemv_t<MP, RW, 16, NESTED>(p, stream); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// rows of W per row group of waves, by M: one group at M <= 4, where x is
+// cheap to restage, else 2 (M <= 16) or 4 (M <= 32) groups share the x chunk
+int gemv_row_groups(int64_t M) { return M <= 4 ? 1 : (M <= 16 ? 2 : 4); }
+
 }  // namespace
 
+// plan fields for the streaming forward: bm = MFMA rows (16 / 32), bn = row
+// groups per workgroup (RW), consumers = contraction slices per row group (KW)
 void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   pl.small_m = true;
   pl.bm = M <= 16 ? 16 : 32;                  // MFMA rows
-  pl.bn = 0;
-  pl.consumers = 0;
+  const int rw = gemv_row_groups(M);
+  pl.bn = rw;
   const int step = pl.bm == 16 ? 256 : 128;
-  const int max_kc = pl.bm == 16 ? 2048 : 1024;
-  const int64_t row_wgs = (N + 4 * pl.bm - 1) / (4 * pl.bm);
-  // aim for two workgroups per compute unit, each chunk a whole number of steps
-  int64_t want = (2 * static_cast<int64_t>(cus) + row_wgs - 1) / row_wgs;
-  const int64_t max_split = (K + step - 1) / step;
-  if (want < 1) want = 1;
-  if (want > max_split) want = max_split;
-  int64_t kc = (K + want - 1) / want;
+  // largest chunk whose x (M + 1 rows, padded) fits the LDS budget
+  int64_t kx = (kXBudgetBytes / 2 / (M + 1) - 8) / step * step;
+  if (kx < step) kx = step;
+  int64_t z = (K + kx - 1) / kx;
+  // tuning override (documented): NF4_GEMV_Z raises the chunk count
+  const char* oz = getenv("NF4_GEMV_Z");
+  if (oz && atoi(oz) > z) z = atoi(oz);
+  if (z > (K + step - 1) / step) z = (K + step - 1) / step;
+  int64_t kc = (K + z - 1) / z;
   kc = (kc + step - 1) / step * step;
-  if (kc > max_kc) kc = max_kc;
+  z = (K + kc - 1) / kc;
+  const int64_t steps = kc / step;
+  // contraction slices per row group: 4 with one row group, else 2, doubled
+  // while a slice would hold more than 8 steps.  Workgroups of 4-8 waves keep
+  // two or more workgroups on a compute unit, so one workgroup's prologue and
+  // cross-wave sum overlap another's expansion (16-wave workgroups measured up
+  // to 2.4x slower at the same work).
+  const int kw_max = kMaxWaves / rw;
+  int kw = rw == 1 ? 4 : 2;
+  while (kw < 8 && kw < kw_max && steps > 8 * kw) kw *= 2;
+  while (kw > 1 && kw > steps) kw /= 2;         // no idle slices on short contractions
+  (void)cus;
+  // tuning override (documented): NF4_GEMV_KW (1, 2, 4, 8, 16 within kMaxWaves / RW)
+  const char* okw = getenv("NF4_GEMV_KW");
+  if (okw) {
+    const int v = atoi(okw);
+    if ((v == 1 || v == 2 || v == 4 || v == 8 || v == 16) && v <= kw_max) kw = v;
+  }
+  pl.consumers = kw;
   pl.kc = static_cast<int>(kc);
-  pl.splits = static_cast<int>((K + kc - 1) / kc);
+  pl.splits = static_cast<int>(z);
   pl.ws_bytes = pl.splits > 1
                     ? static_cast<size_t>(pl.splits) * static_cast<size_t>(M) * static_cast<size_t>(N) * 4
                     : 0;
@@ -265,11 +392,17 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   p.M = static_cast<int32_t>(M);
   p.splits = plan.splits;
   p.kc = plan.kc;
+  if (gemv_lds_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc) > static_cast<size_t>(kXBudgetBytes + 4096))
+    return hipErrorInvalidValue;
   const bool nested = w.nested();
+  const int kw = plan.consumers;
   if (plan.bm == 16) {
-    return nested ? launch_gemv_t<16, true>(p, stream) : launch_gemv_t<16, false>(p, stream);
+    if (plan.bn == 1) return nested ? launch_kw<16, 1, true>(kw, p, stream) : launch_kw<16, 1, false>(kw, p, stream);
+    if (plan.bn == 2) return nested ? launch_kw<16, 2, true>(kw, p, stream) : launch_kw<16, 2, false>(kw, p, stream);
+    return hipErrorInvalidValue;
   }
-  return nested ? launch_gemv_t<32, true>(p, stream) : launch_gemv_t<32, false>(p, stream);
+  if (plan.bn == 4) return nested ? launch_kw<32, 4, true>(kw, p, stream) : launch_kw<32, 4, false>(kw, p, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace nf4
