@@ -7,6 +7,14 @@ HBM-traffic figure back for the benchmark line.  Needs no GPU.
     python -m nf4_bit_weight_amd.profiling stats  <kernel_stats.csv> <out.md> "<command>"
     python -m nf4_bit_weight_amd.profiling traffic <fetch_counter_collection.csv>
            <write_counter_collection.csv> <copy_bytes> <ops> <out.md> "<shape>" "<command>"
+    python -m nf4_bit_weight_amd.profiling mfma <counter_collection.csv> <flops_per_op>
+           <out.md> "<shape>" "<command>"
+
+MFMA: one rocprofv3 run collecting the derived MfmaUtil and VALUBusy metrics
+(percent of the dispatch's active cycles in which the MFMA unit, resp. the
+vector ALU, was busy, averaged over SIMDs / CUs) and SQ_INSTS_VALU_MFMA_MOPS_BF16
+(bf16 MFMA work in units of 512 flops), averaged over the fused matmul
+dispatches; the counted flops are checked against 2 M N K.
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 run
 each) summed over the dispatches of the measured operation (the fused GEMM
@@ -25,9 +33,10 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/nf4_gemm.hip", "csrc/nf4_device.hpp")
+KERNEL_SOURCES = ("csrc/nf4_gemm.hip", "csrc/nf4_gemv.hip", "csrc/nf4_device.hpp")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_gemv<", "k_splitk_reduce")
+FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_splitk_reduce")
+MFMA_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<")
 
 
 def kernel_source_sha256() -> str:
@@ -133,6 +142,54 @@ def summarize_traffic(fetch_csv, write_csv, copy_bytes, ops, out_md, shape, comm
     return fig
 
 
+def mfma_figures(pmc_csv: str, flops_per_op: float) -> dict:
+    util = _per_dispatch(pmc_csv, "MfmaUtil")
+    valu = _per_dispatch(pmc_csv, "VALUBusy")
+    mops = _per_dispatch(pmc_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    ids = [d for d, (n, _) in util.items() if any(k in n for k in MFMA_KERNELS)]
+    if not ids:
+        raise RuntimeError(f"{pmc_csv}: no fused matmul dispatches")
+    names = sorted({_short(util[d][0]) for d in ids})
+    avg = lambda m: sum(m[d][1] for d in ids if d in m) / max(1, sum(1 for d in ids if d in m))
+    flops = avg(mops) * 512.0
+    return {
+        "kernels": names, "dispatches": len(ids),
+        "MfmaUtil_pct": round(avg(util), 2), "VALUBusy_pct": round(avg(valu), 2),
+        "bf16_mfma_flops_per_dispatch": round(flops),
+        "algorithmic_flops_per_op": round(flops_per_op),
+        "counted_over_algorithmic": round(flops / flops_per_op, 4) if flops_per_op else None,
+    }
+
+
+def summarize_mfma(pmc_csv, flops_per_op, out_md, shape, command) -> dict:
+    fig = mfma_figures(pmc_csv, float(flops_per_op))
+    fig["shape"] = shape
+    fig["kernel_source_sha256"] = kernel_source_sha256()
+    lines = [
+        f"# MFMA utilisation of the fused NF4 GEMM: {shape}",
+        "",
+        "One rocprofv3 counter run (MfmaUtil, VALUBusy, SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) of:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "MfmaUtil is the share of the dispatch's active cycles in which a SIMD's MFMA unit was "
+        "busy, averaged over all SIMDs; it is the counter form of the fraction of the bf16 dense "
+        "peak reached while the kernel runs. Counter runs serialise dispatches, so durations are "
+        "taken from the kernel-trace statistics, not from this run. A split contraction runs "
+        "inside the one fused dispatch (its fixed-order reduction is a separate, MFMA-free dispatch), "
+        "so each fused dispatch counts the whole 2 M N K.",
+        "",
+        "```json",
+        json.dumps(fig, indent=1),
+        "```",
+    ]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return fig
+
+
 def read_traffic(md_path: str):
     """The figures of a traffic summary, or None when the file is missing or
     was measured on other kernel sources."""
@@ -152,6 +209,8 @@ def read_traffic(md_path: str):
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         summarize_stats(argv[1], argv[2], argv[3])
+    elif len(argv) >= 6 and argv[0] == "mfma":
+        print(json.dumps(summarize_mfma(argv[1], float(argv[2]), argv[3], argv[4], argv[5])))
     elif len(argv) >= 8 and argv[0] == "traffic":
         fig = summarize_traffic(argv[1], argv[2], int(argv[3]), int(argv[4]), argv[5], argv[6], argv[7])
         print(json.dumps(fig))
