@@ -41,6 +41,15 @@ namespace {
 constexpr int kPD = 4;                    // packed-weight prefetch distance (steps)
 constexpr int kXBudgetBytes = 64 * 1024;  // LDS for the staged x chunk (M + 1 rows)
 constexpr int kMaxWaves = 16;
+// MP = 16: one step of a wave is 16 W rows x 128 contiguous bytes.  The packed
+// bytes are fetched line by line (lane l: 16-byte piece l % 8 of row l / 8,
+// then of row 8 + l / 8), so every load instruction covers 8 whole 128-byte
+// lines; a wave-private LDS buffer (rows padded to 144 bytes against bank
+// conflicts) hands each lane its own block's 32 bytes.  Measured: fetching a
+// block per lane instead (every line split over two instructions) halves the
+// achieved HBM rate of the weight stream.
+constexpr int kTRowPitch = 144;
+constexpr int kTBufBytes = 16 * kTRowPitch;
 
 struct GemvParams {
   const uint16_t* x;     // [M, K] bf16
@@ -50,6 +59,7 @@ struct GemvParams {
   int32_t M;
   int32_t splits;
   int32_t kc;            // contraction per chunk (multiple of the step)
+  int32_t tb_off;        // byte offset of the per-wave line buffers in dynamic LDS (MP = 16)
 };
 
 template <int MP>
@@ -114,33 +124,70 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 
   struct Raw {
     u32x4_t pk0, pk1;
-    uint32_t sc;      // u8 nested index or fp32 bits of the plain absmax
-    float s2;
-    bool valid;
   };
-  // local step ls of this wave; past the end it reloads the last step (an
-  // address already read), so every load stays inside the tensor
+  // The block scales of a batch of kPD steps are loaded one batch ahead and
+  // before that batch's packed bytes, and decoded at the batch's start: a
+  // wait for them then leaves the packed prefetch in flight.  (Carried per
+  // step instead, the compiler narrows the loop-carried absmax byte and
+  // widens it at the loop top, which waits for the newest loads.)
+  struct Scales {
+    uint32_t sc[kPD];  // u8 nested index or fp32 bits of the plain absmax
+    float s2[kPD];
+  };
+  // local step ls of this wave, clamped: past the end it reloads the last
+  // step (an address already read), so every load stays inside the tensor
+  auto clamp_step = [&](int ls) { return s_begin + (ls < nw ? ls : (nw > 0 ? nw - 1 : 0)); };
+  auto step_valid = [&](int ls) {
+    const int64_t koff = k0 + static_cast<int64_t>(S::kStepK) * clamp_step(ls) + 64 * g;
+    return row_ok & (koff < k1) & (nw > 0);
+  };
+  auto load_scales = [&](int ls0, Scales& sq) {
+#pragma unroll
+    for (int j = 0; j < kPD; ++j) {
+      const int64_t koff = k0 + static_cast<int64_t>(S::kStepK) * clamp_step(ls0 + j) + 64 * g;
+      const bool v = row_ok & (koff < k1) & (nw > 0);
+      const uint64_t bb = v ? static_cast<uint64_t>(row_base + koff) >> 6 : 0;
+      if constexpr (NESTED) {
+        sq.sc[j] = static_cast<const uint8_t*>(p.w.absmax)[bb];
+        sq.s2[j] = p.w.nested_absmax[bb >> 8];
+      } else {
+        sq.sc[j] = __float_as_uint(static_cast<const float*>(p.w.absmax)[bb]);
+        sq.s2[j] = 0.f;
+      }
+    }
+  };
   auto load = [&](int ls, Raw& q) {
-    const int sc_ = s_begin + (ls < nw ? ls : (nw > 0 ? nw - 1 : 0));
-    const int64_t koff = k0 + static_cast<int64_t>(S::kStepK) * sc_ + 64 * g;
-    q.valid = row_ok & (koff < k1) & (nw > 0);
-    const uint64_t flat = q.valid ? static_cast<uint64_t>(row_base + koff) : 0;   // multiple of 64
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + (flat >> 1));
-    q.pk0 = src[0];
-    q.pk1 = src[1];
-    const uint64_t b = flat >> 6;
-    if constexpr (NESTED) {
-      q.sc = static_cast<const uint8_t*>(p.w.absmax)[b];
-      q.s2 = p.w.nested_absmax[b >> 8];
+    const int64_t kstep = k0 + static_cast<int64_t>(S::kStepK) * clamp_step(ls);
+    if constexpr (MP == 16) {
+      // whole lines: piece pc of rows lr and 8 + lr of the row group (pieces
+      // of blocks past the end, or rows past N, read the tensor's first bytes;
+      // their consumers see a zero scale)
+      const int lr = lane >> 3, pc = lane & 7;
+      const int64_t nA = (static_cast<int64_t>(blockIdx.x) * RW + rw) * MP + lr;
+      const int64_t kp = kstep + 32 * pc;
+      const bool okk = (kp < k1) & (nw > 0);
+      const uint64_t fa = (okk & (nA < N)) ? static_cast<uint64_t>(nA * K + kp) : 0;
+      const uint64_t fb = (okk & (nA + 8 < N)) ? static_cast<uint64_t>((nA + 8) * K + kp) : 0;
+      q.pk0 = *reinterpret_cast<const u32x4_t*>(p.w.packed + (fa >> 1));
+      q.pk1 = *reinterpret_cast<const u32x4_t*>(p.w.packed + (fb >> 1));
     } else {
-      q.sc = __float_as_uint(static_cast<const float*>(p.w.absmax)[b]);
-      q.s2 = 0.f;
+      const int64_t koff = kstep + 64 * g;
+      const bool v = row_ok & (koff < k1) & (nw > 0);
+      const uint64_t flat = v ? static_cast<uint64_t>(row_base + koff) : 0;   // multiple of 64
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + (flat >> 1));
+      q.pk0 = src[0];
+      q.pk1 = src[1];
     }
   };
 
   // The fences keep every prefetch where it is written: without them the
-  // compiler sinks each load next to its use one iteration later.
-  auto fence = [] { asm volatile("" ::: "memory"); };
+  // compiler sinks each load next to its use one iteration later; the
+  // scheduling barrier keeps any arithmetic on a prefetched register from
+  // moving ahead of its own step (a hoisted use waits for that load).
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // ---- prologue: every load that the first step needs is issued before the
   // first wait, in the order it is consumed (loads complete in order) --------
@@ -164,33 +211,41 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   const int c8n = kc / 8;
   const int nchunks = (M + 1) * c8n;
   u32x4_t xd[kXB];
+  int xm[kXB], x8[kXB];
+  // chunk c -> (row c / c8n, column group c % c8n) without an integer divide:
+  // a float reciprocal, then one correction each way (c < 2^24)
+  const float inv_c8n = 1.0f / static_cast<float>(c8n);
   auto xload = [&](int base) {
 #pragma unroll
     for (int j = 0; j < kXB; ++j) {
       const int c = base + tid + j * kThr;
+      int m = static_cast<int>(static_cast<float>(c) * inv_c8n);
+      m -= (m * c8n > c) ? 1 : 0;
+      m += ((m + 1) * c8n <= c) ? 1 : 0;
+      xm[j] = c < nchunks ? m : M + 1;               // M + 1: no chunk
+      x8[j] = c - m * c8n;
       xd[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (c < nchunks) {
-        const int m = c / c8n, c8 = c - m * c8n;
-        const int64_t k = k0 + 8 * c8;
-        if (m < M && k < K) xd[j] = *reinterpret_cast<const u32x4_t*>(p.x + static_cast<int64_t>(m) * K + k);
-      }
+      const int64_t k = k0 + 8 * x8[j];
+      if (xm[j] < M && k < K)
+        xd[j] = *reinterpret_cast<const u32x4_t*>(p.x + static_cast<int64_t>(xm[j]) * K + k);
     }
   };
   auto xstore = [&](int base) {
+    (void)base;
 #pragma unroll
     for (int j = 0; j < kXB; ++j) {
-      const int c = base + tid + j * kThr;
-      if (c < nchunks) {
-        const int m = c / c8n, c8 = c - m * c8n;
+      if (xm[j] <= M) {
         const u32x4_t d = xd[j];
         const u32x4_t o = {perm(d[1], d[0], 0x05040100u), perm(d[3], d[2], 0x05040100u),
                            perm(d[1], d[0], 0x07060302u), perm(d[3], d[2], 0x07060302u)};
-        *reinterpret_cast<u32x4_t*>(xs + m * pitch + 8 * c8) = o;
+        *reinterpret_cast<u32x4_t*>(xs + xm[j] * pitch + 8 * x8[j]) = o;
       }
     }
   };
   xload(0);
   fence();
+  Scales sc_cur, sc_next;
+  load_scales(0, sc_cur);
   Raw q0, q1, q2, q3;
   load(0, q0);
   load(1, q1);
@@ -217,20 +272,41 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 
   // A fragment of MFMA t in step s: x row r (rows >= M read the zero row M)
   const uint16_t* xrow = xs + (r < M ? r : M) * pitch + 64 * g;
-  auto step = [&](int ls, const Raw& q) {
+  uint8_t* const tbuf = reinterpret_cast<uint8_t*>(xs) + p.tb_off + wave * kTBufBytes;
+  // decoded scale of each step of the current batch (zero for blocks past the ends)
+  float a_dec[kPD];
+  auto decode = [&](int ls0, const Scales& sq) {
+#pragma unroll
+    for (int j = 0; j < kPD; ++j) {
+      float a;
+      if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[sq.sc[j]], sq.s2[j]), off);
+      else a = __uint_as_float(sq.sc[j]);
+      a_dec[j] = step_valid(ls0 + j) ? a : 0.f;
+    }
+  };
+  auto step = [&](int ls, int j, const Raw& q) {
     // all eight A fragments first: their LDS latency overlaps the table build
     const uint16_t* xa = xrow + S::kStepK * (s_begin + ls);
     bf16x8_t afr[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) afr[t] = *reinterpret_cast<const bf16x8_t*>(xa + 8 * t);
-    float a;
-    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[q.sc], q.s2), off);
-    else a = __uint_as_float(q.sc);
-    const Lut lt = make_lut(code, q.valid ? a : 0.f);
+    // the packed registers are redefined at the step's start, so no
+    // arithmetic on them is scheduled (and waited for) earlier
+    u32x4_t d0 = q.pk0, d1 = q.pk1;
+    asm volatile("" : "+v"(d0), "+v"(d1));
+    if constexpr (MP == 16) {
+      // through the wave's line buffer: rows lr and 8 + lr in, block g of row r out
+      const int lr = lane >> 3, pc = lane & 7;
+      *reinterpret_cast<u32x4_t*>(tbuf + lr * kTRowPitch + 16 * pc) = d0;
+      *reinterpret_cast<u32x4_t*>(tbuf + (8 + lr) * kTRowPitch + 16 * pc) = d1;
+      d0 = *reinterpret_cast<const u32x4_t*>(tbuf + r * kTRowPitch + 32 * g);
+      d1 = *reinterpret_cast<const u32x4_t*>(tbuf + r * kTRowPitch + 32 * g + 16);
+    }
+    const Lut lt = make_lut(code, a_dec[j]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint32_t o[4];
-      expand8_eo(t < 4 ? q.pk0[t] : q.pk1[t - 4], lt, o);
+      expand8_eo(t < 4 ? d0[t] : d1[t - 4], lt, o);
       const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
       if constexpr (MP == 16) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[t], bfr, acc, 0, 0, 0);
@@ -242,26 +318,34 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 
   int s = 0;
   for (; s + kPD <= nw; s += kPD) {
-    step(s, q0);
+    decode(s, sc_cur);
+    fence();
+    load_scales(s + kPD, sc_next);
+    fence();
+    step(s, 0, q0);
     fence();
     load(s + 4, q0);
     fence();
-    step(s + 1, q1);
+    step(s + 1, 1, q1);
     fence();
     load(s + 5, q1);
     fence();
-    step(s + 2, q2);
+    step(s + 2, 2, q2);
     fence();
     load(s + 6, q2);
     fence();
-    step(s + 3, q3);
+    step(s + 3, 3, q3);
     fence();
     load(s + 7, q3);
     fence();
+    sc_cur = sc_next;
   }
-  if (s < nw) step(s, q0);
-  if (s + 1 < nw) step(s + 1, q1);
-  if (s + 2 < nw) step(s + 2, q2);
+  if (s < nw) {
+    decode(s, sc_cur);
+    step(s, 0, q0);
+    if (s + 1 < nw) step(s + 1, 1, q1);
+    if (s + 2 < nw) step(s + 2, 2, q2);
+  }
 
   // ---- fixed-order sum over the KW contraction slices of each row group ------
   if constexpr (KW > 1) {
@@ -296,10 +380,14 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 }
 
 // LDS of one launch: the x chunk (M + 1 rows) or the cross-wave sums, whichever is larger
-size_t gemv_lds_bytes(int mp, int rw, int kw, int64_t M, int kc) {
+size_t gemv_region_bytes(int mp, int rw, int kw, int64_t M, int kc) {
   const size_t xb = static_cast<size_t>(M + 1) * static_cast<size_t>(kc + 8) * 2;
   const size_t rb = static_cast<size_t>(kw - 1) * rw * (mp == 16 ? 4 : 16) * 64 * 4;
-  return xb > rb ? xb : rb;
+  return ((xb > rb ? xb : rb) + 15) / 16 * 16;
+}
+// plus the per-wave line buffers (MP = 16)
+size_t gemv_lds_bytes(int mp, int rw, int kw, int64_t M, int kc) {
+  return gemv_region_bytes(mp, rw, kw, M, kc) + (mp == 16 ? static_cast<size_t>(rw) * kw * kTBufBytes : 0);
 }
 
 template <int MP, int RW, int KW, bool NESTED>
@@ -307,7 +395,8 @@ hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
   auto kern = k_gemv<MP, RW, KW, NESTED>;
   static const bool attr_done = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kXBudgetBytes + 4096);
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kXBudgetBytes + 4096 + kMaxWaves * kTBufBytes);
     (void)hipGetLastError();
     return true;
   }();
@@ -392,8 +481,10 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   p.M = static_cast<int32_t>(M);
   p.splits = plan.splits;
   p.kc = plan.kc;
-  if (gemv_lds_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc) > static_cast<size_t>(kXBudgetBytes + 4096))
+  if (gemv_lds_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc) >
+      static_cast<size_t>(kXBudgetBytes + 4096 + kMaxWaves * kTBufBytes))
     return hipErrorInvalidValue;
+  p.tb_off = static_cast<int32_t>(gemv_region_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc));
   const bool nested = w.nested();
   const int kw = plan.consumers;
   if (plan.bm == 16) {
