@@ -595,8 +595,19 @@ struct PP {
   static constexpr int kThreads = 512;
   static constexpr int MI = 4, NI = 2, WM = 128, WN = 64, KK = 4;
   static constexpr int kAElems = BM * BK;
-  static constexpr int kBTPitch = BN + 16;
+  // Input gradient: the expanded tile is [k-row][n] with 256-element rows
+  // and its 16-byte units XOR-swizzled by the row: unit c of row r is stored
+  // at unit c ^ swz_t(r).  Both the expansion's 16-byte writes (16 lanes: 8
+  // rows x 2 halves) and the transposed 8-byte fragment reads (32 lanes: 4
+  // rows x 8 columns) then hit 64 distinct banks; a padded pitch (BN + 16)
+  // left both 2-way conflicted (measured: conflict cycles were a third of the
+  // kernel's LDS cycles).
+  static constexpr int kBTPitch = BN;
   static constexpr int kWSlot = 10240;          // 8 KB packed, 1 KB scales, 1 KB nested scales
+  // unit swizzle of row r: rows r & 3 = 0..3 take distinct bits 2-3 (reads
+  // of four rows), and over r & 7 the values with bit 2 cleared are distinct
+  // (writes of eight rows, two halves 4 units apart)
+  static __device__ __forceinline__ int swz_t(int r) { return (5 * (r & 3)) ^ (2 * ((r >> 2) & 1)); }
   template <bool TRANS>
   static constexpr int b_elems() { return TRANS ? BK * kBTPitch : BN * BK; }
   template <bool TRANS>
@@ -774,7 +785,8 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
 #undef NF4_PP_READ
   auto b_dst = [&](int buf, int d) -> uint16_t* {
     if constexpr (TRANS) {
-      return b_tile(buf) + (u % 64) * PP::kBTPitch + 64 * (u / 64) + 32 * hh + 8 * d;
+      const int row = u % 64, unit = 8 * (u / 64) + 4 * hh + d;
+      return b_tile(buf) + row * PP::kBTPitch + 8 * (unit ^ PP::swz_t(row));
     } else {
       return b_tile(buf) + u * BK + 8 * swz(u, 4 * hh + d);
     }
@@ -826,21 +838,30 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   const int y = h ^ ((r32 >> 1) & 7);
   const char* pa[4];
   const char* pb[4];
+  const char* pbt[PP::NI][2];     // input gradient: fragment j, rows +0 / +4
   {
     const char* a0 = reinterpret_cast<const char*>(lds) + (wm * PP::WM + r32) * BK * 2;
     const char* b0 = reinterpret_cast<const char*>(lds) + kBOff;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       pa[q] = a0 + 16 * ((2 * q) ^ y);
-      if constexpr (TRANS) {
-        const int tg = lane >> 4, ts = lane & 15;
-        const int tr_row = 8 * (tg >> 1) + (ts >> 2);
-        const int tr_col = wn * PP::WN + 16 * (tg & 1) + 4 * (ts & 3);
-        pb[q] = b0 + (tr_row * PP::kBTPitch + tr_col) * 2;
-      } else {
-        pb[q] = b0 + (wn * PP::WN + r32) * BK * 2 + 16 * ((2 * q) ^ y);
-      }
+      if constexpr (!TRANS) pb[q] = b0 + (wn * PP::WN + r32) * BK * 2 + 16 * ((2 * q) ^ y);
     }
+    if constexpr (TRANS) {
+      // lane: row 8*(tg/2) + ts/4 (+4 for the upper half, +16 per k-slice,
+      // which keeps row & 7), columns 16*(tg&1) + 4*(ts&3) of fragment j
+      const int tg = lane >> 4, ts = lane & 15;
+      const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+      const int tr_col = wn * PP::WN + 16 * (tg & 1) + 4 * (ts & 3);
+#pragma unroll
+      for (int j = 0; j < PP::NI; ++j)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int row = tr_row + 4 * hf, col = tr_col + 32 * j;
+          pbt[j][hf] = b0 + (row * PP::kBTPitch + 8 * ((col >> 3) ^ PP::swz_t(row)) + (col & 7)) * 2;
+        }
+    }
+    (void)pb;
   }
   struct Frags {
     bf16x8_t a[PP::MI];
@@ -853,9 +874,9 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < PP::NI; ++j) {
       if constexpr (TRANS) {
-        const char* src = pb[0] + buf * kBElems * 2 + (16 * kk * PP::kBTPitch + 32 * j) * 2;
-        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * PP::kBTPitch * 2));
+        const int off = (buf * kBElems + 16 * kk * PP::kBTPitch) * 2;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pbt[j][0] + off));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pbt[j][1] + off));
         u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
         f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
       } else {
