@@ -9,6 +9,7 @@ HBM-traffic figure back for the benchmark line.  Needs no GPU.
            <write_counter_collection.csv> <copy_bytes> <ops> <out.md> "<shape>" "<command>"
     python -m nf4_bit_weight_amd.profiling mfma <counter_collection.csv> <flops_per_op>
            <out.md> "<shape>" "<command>"
+    python -m nf4_bit_weight_amd.profiling lds <counter_collection.csv> <out.md> "<shape>" "<command>"
 
 MFMA: one rocprofv3 run collecting the derived MfmaUtil and VALUBusy metrics
 (percent of the dispatch's active cycles in which the MFMA unit, resp. the
@@ -190,6 +191,52 @@ def summarize_mfma(pmc_csv, flops_per_op, out_md, shape, command) -> dict:
     return fig
 
 
+def lds_figures(pmc_csv: str) -> dict:
+    """LDS counters averaged over the fused matmul dispatches, and the derived
+    bank-conflict ratio (conflict cycles over conflict-free active cycles, the
+    form of rocprofv3's LdsBankConflict metric)."""
+    names = ("SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT",
+             "SQ_LDS_UNALIGNED_STALL", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS")
+    per = {c: _per_dispatch(pmc_csv, c) for c in names}
+    ids = [d for d, (n, _) in per["SQ_LDS_IDX_ACTIVE"].items() if any(k in n for k in MFMA_KERNELS)]
+    if not ids:
+        raise RuntimeError(f"{pmc_csv}: no fused matmul dispatches")
+    avg = {c: sum(per[c][d][1] for d in ids if d in per[c]) / len(ids) for c in names}
+    act, bc = avg["SQ_LDS_IDX_ACTIVE"], avg["SQ_LDS_BANK_CONFLICT"]
+    return {
+        "kernels": sorted({_short(per["SQ_LDS_IDX_ACTIVE"][d][0]) for d in ids}),
+        "dispatches": len(ids),
+        **{c: round(v) for c, v in avg.items()},
+        "bank_conflict_ratio": round(bc / (act - bc), 4) if act > bc else None,
+    }
+
+
+def summarize_lds(pmc_csv, out_md, shape, command) -> dict:
+    fig = lds_figures(pmc_csv)
+    fig["shape"] = shape
+    fig["kernel_source_sha256"] = kernel_source_sha256()
+    lines = [
+        f"# LDS counters of the fused NF4 GEMM: {shape}",
+        "",
+        "One rocprofv3 counter run of:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "Per-dispatch averages over the fused matmul dispatches. bank_conflict_ratio is "
+        "SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT): extra LDS cycles "
+        "spent on bank conflicts per conflict-free LDS cycle.",
+        "",
+        "```json",
+        json.dumps(fig, indent=1),
+        "```",
+    ]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return fig
+
+
 def read_traffic(md_path: str):
     """The figures of a traffic summary, or None when the file is missing or
     was measured on other kernel sources."""
@@ -209,6 +256,8 @@ def read_traffic(md_path: str):
 def main(argv):
     if len(argv) >= 4 and argv[0] == "stats":
         summarize_stats(argv[1], argv[2], argv[3])
+    elif len(argv) >= 5 and argv[0] == "lds":
+        print(json.dumps(summarize_lds(argv[1], argv[2], argv[3], argv[4])))
     elif len(argv) >= 6 and argv[0] == "mfma":
         print(json.dumps(summarize_mfma(argv[1], float(argv[2]), argv[3], argv[4], argv[5])))
     elif len(argv) >= 8 and argv[0] == "traffic":
