@@ -20,9 +20,13 @@
 //   * The contraction is permuted inside each step so that a lane's k-group
 //     is one whole NF4 block: lane (n = l % MP, g = l / MP) of MFMA t reads
 //     k = 64 * (G * s + g) + 8 t .. + 7 of step s (G = 64 / MP blocks).  A
-//     lane thus loads its block's 32 packed bytes with two 16-byte loads (the
-//     G lanes of one row read G consecutive blocks: whole 128-byte lines),
-//     builds one 16-entry byte table per block and expands one dword per MFMA.
+//     lane builds one 16-entry byte table per block and expands one dword of
+//     its block's 32 packed bytes per MFMA.  At MP = 16 the packed bytes are
+//     fetched as whole 128-byte lines (8 lanes per line) and handed to their
+//     lanes through a per-wave LDS buffer; at MP = 32 each lane loads its own
+//     block with two 16-byte loads.
+//   * Block scales are loaded a batch of PD steps ahead of that batch's
+//     packed bytes and decoded at the batch start.
 //   * Within each 8-element group the expansion emits the order
 //     (0, 2, 4, 6, 1, 3, 5, 7), which saves the final interleave; x is staged
 //     into LDS in the same order, so every product pairs the right elements.

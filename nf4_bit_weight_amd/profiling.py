@@ -40,13 +40,39 @@ FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_splitk_reduce")
 MFMA_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (string and
+    character literals kept), so that a comment edit keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == "/" and i + 1 < n and text[i + 1] == "/":
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif c == "/" and i + 1 < n and text[i + 1] == "*":
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha256() -> str:
-    """Hash of the sources the fused GEMM is built from: a traffic figure
-    taken from counters is valid only for the kernel it was measured on."""
+    """Hash of the code (comments and layout excluded) the fused kernels are
+    built from: a traffic figure taken from counters is valid only for the
+    kernel it was measured on."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(PKG, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
