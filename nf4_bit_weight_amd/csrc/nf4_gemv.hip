@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   }
   // x[:, k0:k0+kc] is staged in batches of kXB 16-byte chunks per thread; each
   // 8-group is stored as (0,2,4,6,1,3,5,7); row M and columns >= K are zero
-  constexpr int kXB = 4;
+  constexpr int kXB = RW == 1 ? 4 : 8;       // more rows per workgroup: larger batches
   const int c8n = kc / 8;
   const int nchunks = (M + 1) * c8n;
   u32x4_t xd[kXB];
@@ -425,10 +425,6 @@ hipError_t launch_kw(int kw, const GemvParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-// rows of W per row group of waves, by M: one group at M <= 4, where x is
-// cheap to restage, else 2 (M <= 16) or 4 (M <= 32) groups share the x chunk
-int gemv_row_groups(int64_t M) { return M <= 4 ? 1 : (M <= 16 ? 2 : 4); }
-
 }  // namespace
 
 // plan fields for the streaming forward: bm = MFMA rows (16 / 32), bn = row
@@ -436,8 +432,6 @@ int gemv_row_groups(int64_t M) { return M <= 4 ? 1 : (M <= 16 ? 2 : 4); }
 void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   pl.small_m = true;
   pl.bm = M <= 16 ? 16 : 32;                  // MFMA rows
-  const int rw = gemv_row_groups(M);
-  pl.bn = rw;
   const int step = pl.bm == 16 ? 256 : 128;
   // largest chunk whose x (M + 1 rows, padded) fits the LDS budget
   int64_t kx = (kXBudgetBytes / 2 / (M + 1) - 8) / step * step;
@@ -451,6 +445,24 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   kc = (kc + step - 1) / step * step;
   z = (K + kc - 1) / kc;
   const int64_t steps = kc / step;
+  // Row groups per workgroup: each shares one staged x chunk.  At M <= 4 the
+  // chunk is two rows and one group is best; at M = 5..16 the largest of 4 /
+  // 2 / 1 groups that still gives 1.5 workgroups per compute unit (measured:
+  // 4 groups take the gate projection at M = 16 from 24.8 to 19.9 us, but
+  // slow the q projection, which then has too few workgroups); M > 16: 4.
+  int rw = 1;
+  if (M > 16) {
+    rw = 4;
+  } else if (M > 4) {
+    for (int c = 4; c >= 1; c /= 2) {
+      const int64_t wgs_c = (N + 16 * c - 1) / (16 * c) * z;
+      if (2 * wgs_c >= 3 * static_cast<int64_t>(cus) || c == 1) { rw = c; break; }
+    }
+  }
+  // tuning override (documented): NF4_GEMV_RW (row groups per workgroup: 1 / 2 / 4 at M <= 16)
+  const char* orw = getenv("NF4_GEMV_RW");
+  if (orw && M <= 16 && (atoi(orw) == 1 || atoi(orw) == 2 || atoi(orw) == 4)) rw = atoi(orw);
+  pl.bn = rw;
   // contraction slices per row group: 4 with one row group, else 2, doubled
   // while a slice would hold more than 8 steps.  Workgroups of 4-8 waves keep
   // two or more workgroups on a compute unit, so one workgroup's prologue and
@@ -460,7 +472,6 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   int kw = rw == 1 ? 4 : 2;
   while (kw < 8 && kw < kw_max && steps > 8 * kw) kw *= 2;
   while (kw > 1 && kw > steps) kw /= 2;         // no idle slices on short contractions
-  (void)cus;
   // tuning override (documented): NF4_GEMV_KW (1, 2, 4, 8, 16 within kMaxWaves / RW)
   const char* okw = getenv("NF4_GEMV_KW");
   if (okw) {
@@ -494,6 +505,7 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   if (plan.bm == 16) {
     if (plan.bn == 1) return nested ? launch_kw<16, 1, true>(kw, p, stream) : launch_kw<16, 1, false>(kw, p, stream);
     if (plan.bn == 2) return nested ? launch_kw<16, 2, true>(kw, p, stream) : launch_kw<16, 2, false>(kw, p, stream);
+    if (plan.bn == 4) return nested ? launch_kw<16, 4, true>(kw, p, stream) : launch_kw<16, 4, false>(kw, p, stream);
     return hipErrorInvalidValue;
   }
   if (plan.bn == 4) return nested ? launch_kw<32, 4, true>(kw, p, stream) : launch_kw<32, 4, false>(kw, p, stream);
