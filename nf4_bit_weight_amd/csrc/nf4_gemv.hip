@@ -94,10 +94,12 @@ __device__ __forceinline__ void expand8_eo(uint32_t p, const Lut& t, uint32_t (&
   out[3] = perm(ho, lo, 0x07030602u);
 }
 
-template <int MP, int RW, int KW, bool NESTED>
+template <int MP, int RW, int KW, bool NESTED, int MH>
 __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   using S = Gv<MP>;
+  static_assert(MH == 1 || MP == 16, "two x halves only with 16-row groups");
   constexpr int kThr = 64 * RW * KW;
+  constexpr int kRegs = S::kAccRegs * MH;       // accumulator registers per lane
   // [M + 1][kc + 8] bf16 (row M is zero), reused for the cross-wave sums
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ float sncode[256];
@@ -270,12 +272,17 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   }
   __syncthreads();
 
-  acc_t<MP> acc;
+  acc_t<MP> acc[MH];
 #pragma unroll
-  for (int i = 0; i < S::kAccRegs; ++i) acc[i] = 0.f;
+  for (int h = 0; h < MH; ++h)
+#pragma unroll
+    for (int i = 0; i < S::kAccRegs; ++i) acc[h][i] = 0.f;
 
   // A fragment of MFMA t in step s: x row r (rows >= M read the zero row M)
-  const uint16_t* xrow = xs + (r < M ? r : M) * pitch + 64 * g;
+  // x rows r (and r + 16 for the second half at M > 16); rows >= M read the zero row M
+  const uint16_t* xrow[MH];
+#pragma unroll
+  for (int h = 0; h < MH; ++h) xrow[h] = xs + (r + 16 * h < M ? r + 16 * h : M) * pitch + 64 * g;
   uint8_t* const tbuf = reinterpret_cast<uint8_t*>(xs) + p.tb_off + wave * kTBufBytes;
   // decoded scale of each step of the current batch (zero for blocks past the ends)
   float a_dec[kPD];
@@ -290,10 +297,12 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   };
   auto step = [&](int ls, int j, const Raw& q) {
     // all eight A fragments first: their LDS latency overlaps the table build
-    const uint16_t* xa = xrow + S::kStepK * (s_begin + ls);
+    const int xo = S::kStepK * (s_begin + ls);
     bf16x8_t afr[8];
+    if constexpr (MH == 1) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) afr[t] = *reinterpret_cast<const bf16x8_t*>(xa + 8 * t);
+      for (int t = 0; t < 8; ++t) afr[t] = *reinterpret_cast<const bf16x8_t*>(xrow[0] + xo + 8 * t);
+    }
     // the packed registers are redefined at the step's start, so no
     // arithmetic on them is scheduled (and waited for) earlier
     u32x4_t d0 = q.pk0, d1 = q.pk1;
@@ -312,10 +321,16 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
       uint32_t o[4];
       expand8_eo(t < 4 ? d0[t] : d1[t - 4], lt, o);
       const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
-      if constexpr (MP == 16) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[t], bfr, acc, 0, 0, 0);
+      if constexpr (MP == 16 && MH == 1) {
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[t], bfr, acc[0], 0, 0, 0);
+      } else if constexpr (MP == 16) {
+        // the expanded fragment serves both halves of x (fragments read here)
+#pragma unroll
+        for (int h = 0; h < MH; ++h)
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8_t*>(xrow[h] + xo + 8 * t), bfr, acc[h], 0, 0, 0);
       } else {
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[t], bfr, acc, 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[t], bfr, acc[0], 0, 0, 0);
       }
     }
   };
@@ -357,28 +372,35 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
     float* red = reinterpret_cast<float*>(xs);         // [KW-1][RW][regs][64]
     if (kw > 0) {
 #pragma unroll
-      for (int i = 0; i < S::kAccRegs; ++i)
-        red[(((kw - 1) * RW + rw) * S::kAccRegs + i) * 64 + lane] = acc[i];
+      for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int i = 0; i < S::kAccRegs; ++i)
+          red[(((kw - 1) * RW + rw) * kRegs + h * S::kAccRegs + i) * 64 + lane] = acc[h][i];
     }
     __syncthreads();
     if (kw > 0) return;
     for (int v = 1; v < KW; ++v) {
 #pragma unroll
-      for (int i = 0; i < S::kAccRegs; ++i)
-        acc[i] = __fadd_rn(acc[i], red[(((v - 1) * RW + rw) * S::kAccRegs + i) * 64 + lane]);
+      for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int i = 0; i < S::kAccRegs; ++i)
+          acc[h][i] = __fadd_rn(acc[h][i], red[(((v - 1) * RW + rw) * kRegs + h * S::kAccRegs + i) * 64 + lane]);
     }
   }
 
   // ---- epilogue: lane holds output column n; rows as laid out by the MFMA ----
   if (!row_ok) return;
 #pragma unroll
-  for (int i = 0; i < S::kAccRegs; ++i) {
-    const int m = MP == 16 ? 4 * (lane / 16) + i : 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
-    if (m >= M) continue;
-    if (p.splits == 1) {
-      p.y[static_cast<int64_t>(m) * N + n] = to_bf16(acc[i]);
-    } else {
-      p.partial[(static_cast<int64_t>(z) * M + m) * N + n] = acc[i];
+  for (int h = 0; h < MH; ++h) {
+#pragma unroll
+    for (int i = 0; i < S::kAccRegs; ++i) {
+      const int m = MP == 16 ? 16 * h + 4 * (lane / 16) + i : 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+      if (m >= M) continue;
+      if (p.splits == 1) {
+        p.y[static_cast<int64_t>(m) * N + n] = to_bf16(acc[h][i]);
+      } else {
+        p.partial[(static_cast<int64_t>(z) * M + m) * N + n] = acc[h][i];
+      }
     }
   }
 }
@@ -386,7 +408,8 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 // LDS of one launch: the x chunk (M + 1 rows) or the cross-wave sums, whichever is larger
 size_t gemv_region_bytes(int mp, int rw, int kw, int64_t M, int kc) {
   const size_t xb = static_cast<size_t>(M + 1) * static_cast<size_t>(kc + 8) * 2;
-  const size_t rb = static_cast<size_t>(kw - 1) * rw * (mp == 16 ? 4 : 16) * 64 * 4;
+  const int regs = mp == 32 ? 16 : (M > 16 ? 8 : 4);      // x halves at M > 16 (MP = 16)
+  const size_t rb = static_cast<size_t>(kw - 1) * rw * regs * 64 * 4;
   return ((xb > rb ? xb : rb) + 15) / 16 * 16;
 }
 // plus the per-wave line buffers (MP = 16)
@@ -394,9 +417,9 @@ size_t gemv_lds_bytes(int mp, int rw, int kw, int64_t M, int kc) {
   return gemv_region_bytes(mp, rw, kw, M, kc) + (mp == 16 ? static_cast<size_t>(rw) * kw * kTBufBytes : 0);
 }
 
-template <int MP, int RW, int KW, bool NESTED>
+template <int MP, int RW, int KW, bool NESTED, int MH>
 hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
-  auto kern = k_gemv<MP, RW, KW, NESTED>;
+  auto kern = k_gemv<MP, RW, KW, NESTED, MH>;
   static const bool attr_done = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -412,14 +435,14 @@ hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MP, int RW, bool NESTED>
+template <int MP, int RW, bool NESTED, int MH>
 hipError_t launch_kw(int kw, const GemvParams& p, hipStream_t stream) {
   switch (kw) {
-    case 1: return launch_gemv_t<MP, RW, 1, NESTED>(p, stream);
-    case 2: return launch_gemv_t<MP, RW, 2, NESTED>(p, stream);
-    case 4: return launch_gemv_t<MP, RW, 4, NESTED>(p, stream);
-    case 8: if constexpr (RW <= 2) return launch_gemv_t<MP, RW, 8, NESTED>(p, stream); break;
-    case 16: if constexpr (RW == 1) return launch_gemv_t<MP, RW, 16, NESTED>(p, stream); break;
+    case 1: return launch_gemv_t<MP, RW, 1, NESTED, MH>(p, stream);
+    case 2: return launch_gemv_t<MP, RW, 2, NESTED, MH>(p, stream);
+    case 4: return launch_gemv_t<MP, RW, 4, NESTED, MH>(p, stream);
+    case 8: if constexpr (RW <= 2) return launch_gemv_t<MP, RW, 8, NESTED, MH>(p, stream); break;
+    case 16: if constexpr (RW == 1 && MH == 1) return launch_gemv_t<MP, RW, 16, NESTED, MH>(p, stream); break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -431,7 +454,15 @@ hipError_t launch_kw(int kw, const GemvParams& p, hipStream_t stream) {
 // groups per workgroup (RW), consumers = contraction slices per row group (KW)
 void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   pl.small_m = true;
-  pl.bm = M <= 16 ? 16 : 32;                  // MFMA rows
+  // MFMA rows: 16-row W groups up to M = 24 (two halves of x above 16), 32-row
+  // groups from M = 25 (measured over the Llama-3.1-8B projections: per layer
+  // 109 vs 130 us at M = 17, 119 vs 130 us at M = 24, but 143 vs 136 us at
+  // M = 32, where the halves' smaller x chunks cost more partial traffic);
+  // tuning override (documented): NF4_GEMV_MP32=0/1 picks either above M = 16
+  const char* o32 = getenv("NF4_GEMV_MP32");
+  bool mp32 = M > 24;
+  if (o32 && (o32[0] == '0' || o32[0] == '1')) mp32 = o32[0] == '1';
+  pl.bm = (M > 16 && mp32) ? 32 : 16;
   const int step = pl.bm == 16 ? 256 : 128;
   // largest chunk whose x (M + 1 rows, padded) fits the LDS budget
   int64_t kx = (kXBudgetBytes / 2 / (M + 1) - 8) / step * step;
@@ -446,12 +477,12 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   z = (K + kc - 1) / kc;
   const int64_t steps = kc / step;
   // Row groups per workgroup: each shares one staged x chunk.  At M <= 4 the
-  // chunk is two rows and one group is best; at M = 5..16 the largest of 4 /
-  // 2 / 1 groups that still gives 1.5 workgroups per compute unit (measured:
-  // 4 groups take the gate projection at M = 16 from 24.8 to 19.9 us, but
-  // slow the q projection, which then has too few workgroups); M > 16: 4.
+  // chunk is two rows and one group is best; above, the largest of 4 / 2 / 1
+  // groups that still gives 1.5 workgroups per compute unit (measured: 4
+  // groups take the gate projection at M = 16 from 24.8 to 19.9 us, but slow
+  // the q projection, which then has too few workgroups); 32-row groups: 4.
   int rw = 1;
-  if (M > 16) {
+  if (pl.bm == 32) {
     rw = 4;
   } else if (M > 4) {
     for (int c = 4; c >= 1; c /= 2) {
@@ -461,14 +492,15 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   }
   // tuning override (documented): NF4_GEMV_RW (row groups per workgroup: 1 / 2 / 4 at M <= 16)
   const char* orw = getenv("NF4_GEMV_RW");
-  if (orw && M <= 16 && (atoi(orw) == 1 || atoi(orw) == 2 || atoi(orw) == 4)) rw = atoi(orw);
+  if (orw && pl.bm == 16 && (atoi(orw) == 1 || atoi(orw) == 2 || atoi(orw) == 4)) rw = atoi(orw);
   pl.bn = rw;
   // contraction slices per row group: 4 with one row group, else 2, doubled
   // while a slice would hold more than 8 steps.  Workgroups of 4-8 waves keep
   // two or more workgroups on a compute unit, so one workgroup's prologue and
   // cross-wave sum overlap another's expansion (16-wave workgroups measured up
   // to 2.4x slower at the same work).
-  const int kw_max = kMaxWaves / rw;
+  // (two x halves hold twice the accumulators: at most 8 waves per group)
+  const int kw_max = (pl.bm == 16 && M > 16 ? kMaxWaves / 2 : kMaxWaves) / rw;
   int kw = rw == 1 ? 4 : 2;
   while (kw < 8 && kw < kw_max && steps > 8 * kw) kw *= 2;
   while (kw > 1 && kw > steps) kw /= 2;         // no idle slices on short contractions
@@ -502,13 +534,20 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   p.tb_off = static_cast<int32_t>(gemv_region_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc));
   const bool nested = w.nested();
   const int kw = plan.consumers;
-  if (plan.bm == 16) {
-    if (plan.bn == 1) return nested ? launch_kw<16, 1, true>(kw, p, stream) : launch_kw<16, 1, false>(kw, p, stream);
-    if (plan.bn == 2) return nested ? launch_kw<16, 2, true>(kw, p, stream) : launch_kw<16, 2, false>(kw, p, stream);
-    if (plan.bn == 4) return nested ? launch_kw<16, 4, true>(kw, p, stream) : launch_kw<16, 4, false>(kw, p, stream);
+  if (plan.bm == 16 && M > 16) {
+    // 16-row groups, two halves of x per expanded fragment
+    if (plan.bn == 1) return nested ? launch_kw<16, 1, true, 2>(kw, p, stream) : launch_kw<16, 1, false, 2>(kw, p, stream);
+    if (plan.bn == 2) return nested ? launch_kw<16, 2, true, 2>(kw, p, stream) : launch_kw<16, 2, false, 2>(kw, p, stream);
+    if (plan.bn == 4) return nested ? launch_kw<16, 4, true, 2>(kw, p, stream) : launch_kw<16, 4, false, 2>(kw, p, stream);
     return hipErrorInvalidValue;
   }
-  if (plan.bn == 4) return nested ? launch_kw<32, 4, true>(kw, p, stream) : launch_kw<32, 4, false>(kw, p, stream);
+  if (plan.bm == 16) {
+    if (plan.bn == 1) return nested ? launch_kw<16, 1, true, 1>(kw, p, stream) : launch_kw<16, 1, false, 1>(kw, p, stream);
+    if (plan.bn == 2) return nested ? launch_kw<16, 2, true, 1>(kw, p, stream) : launch_kw<16, 2, false, 1>(kw, p, stream);
+    if (plan.bn == 4) return nested ? launch_kw<16, 4, true, 1>(kw, p, stream) : launch_kw<16, 4, false, 1>(kw, p, stream);
+    return hipErrorInvalidValue;
+  }
+  if (plan.bn == 4) return nested ? launch_kw<32, 4, true, 1>(kw, p, stream) : launch_kw<32, 4, false, 1>(kw, p, stream);
   return hipErrorInvalidValue;
 }
 
