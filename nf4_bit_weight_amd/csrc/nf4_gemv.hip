@@ -278,8 +278,8 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 #pragma unroll
     for (int i = 0; i < S::kAccRegs; ++i) acc[h][i] = 0.f;
 
-  // A fragment of MFMA t in step s: x row r (rows >= M read the zero row M)
-  // x rows r (and r + 16 for the second half at M > 16); rows >= M read the zero row M
+  // A fragments of MFMA t: x row r, and r + 16 for the second half at M > 16
+  // (rows >= M read the zero row M)
   const uint16_t* xrow[MH];
 #pragma unroll
   for (int h = 0; h < MH; ++h) xrow[h] = xs + (r + 16 * h < M ? r + 16 * h : M) * pitch + 64 * g;
@@ -296,7 +296,8 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
     }
   };
   auto step = [&](int ls, int j, const Raw& q) {
-    // all eight A fragments first: their LDS latency overlaps the table build
+    // one x half: all eight A fragments first, so their LDS latency overlaps
+    // the table build; two halves: read at their MFMAs (registers)
     const int xo = S::kStepK * (s_begin + ls);
     bf16x8_t afr[8];
     if constexpr (MH == 1) {
