@@ -57,7 +57,8 @@
  *              negative NF4_ERR_* code.  On error nothing is enqueued and no
  *              output is touched.  nf4_status_str() names each code.  No C++
  *              exception crosses this interface.
- *   Empty      M == 0 (or N*K == 0 for the codec) returns NF4_OK with no work.
+ *   Empty      M == 0 (or N*K == 0 for the codec) returns NF4_OK with no work;
+ *              the activation and output pointers may then be NULL.
  *   Determinism  Every kernel sums in a fixed order and uses no atomics; the
  *              split of a contraction across workgroups is a pure function of
  *              (M, N, K, compute-unit count).  Repeated calls with the same

@@ -51,7 +51,9 @@ int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed
   const bool bwd = kind == GemmKind::kBwdInput;
   int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K);
   if (st) return st;
-  if (!A || !C) return NF4_ERR_NULL;
+  // an empty batch reads and writes nothing: its activation and output may be NULL
+  // (as torch gives for empty tensors)
+  if ((!A || !C) && M != 0) return NF4_ERR_NULL;
   st = check_gemm_shape(M, N, K, bwd);
   if (st) return st;
   if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
@@ -83,7 +85,7 @@ int grouped_common(GemmKind kind, const void* A, const int32_t* offsets, int32_t
   int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode,
                    static_cast<int64_t>(E) * N, K);
   if (st) return st;
-  if (!A || !C || !offsets) return NF4_ERR_NULL;
+  if (!offsets || ((!A || !C) && total_M != 0)) return NF4_ERR_NULL;
   st = check_gemm_shape(total_M, N, K, bwd);
   if (st) return st;
   if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;

@@ -84,6 +84,8 @@ def test_matmul_validation(lib):
     assert _fwd(lib, x=MISALIGNED) == L.NF4_ERR_ALIGN
     assert _fwd(lib, packed=MISALIGNED) == L.NF4_ERR_ALIGN
     assert _fwd(lib, M=0) == L.NF4_OK                         # empty: nothing to do
+    assert _fwd(lib, M=0, x=None, y=None) == L.NF4_OK         # empty tensors may be NULL
+    assert _fwd(lib, M=0, packed=None) == L.NF4_ERR_NULL      # the weight is still checked
     bw = lib.nf4_matmul_bwd_input(FAKE, 4, FAKE, FAKE, None, None, FAKE, None, 12, 64, FAKE,
                                   None, 0, None)
     assert bw == L.NF4_ERR_UNSUPPORTED                        # N % 8 for the input grad
@@ -117,6 +119,8 @@ def test_grouped_validation(lib):
     assert g(FAKE, FAKE, 0, 8, FAKE, FAKE, None, None, FAKE, None, 8, 64, FAKE, None, 0, None) == L.NF4_ERR_SHAPE
     assert g(FAKE, None, 2, 8, FAKE, FAKE, None, None, FAKE, None, 8, 64, FAKE, None, 0, None) == L.NF4_ERR_NULL
     assert g(FAKE, FAKE, 2, 8, FAKE, FAKE, None, None, FAKE, None, 8, 96, FAKE, None, 0, None) == L.NF4_ERR_UNSUPPORTED
+    assert g(None, FAKE, 2, 0, FAKE, FAKE, None, None, FAKE, None, 8, 64, None, None, 0, None) == L.NF4_OK
+    assert g(None, FAKE, 2, 4, FAKE, FAKE, None, None, FAKE, None, 8, 64, FAKE, None, 0, None) == L.NF4_ERR_NULL
 
 
 def test_path_counters_host_side(lib):
