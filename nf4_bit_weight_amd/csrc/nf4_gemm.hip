@@ -397,7 +397,13 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
       for (int j = 0; j < PD; ++j) issue_w(j, j);
       wait_vm(ic<(PD - 1) * kW>{});                // every activation copy, weights of step 0
       expand_into(0, 0, 0);
-      wait_vm(ic<(PD - 2) * kW>{});                // weights of step 1
+      // Weights of step 1, and of step 2 when the prologue issued them: kWait
+      // assumes each step's weight copy is followed by the copies of later
+      // steps in the steady order (activation, weights), but the prologue put
+      // every activation copy first, so at the end of step 0 fewer operations
+      // follow the weights of step 2 than kWait allows in flight (with four
+      // activation stages and four weight slots).
+      wait_vm(ic<(PD > 2 ? PD - 3 : 0) * kW>{});
       __syncthreads();
       auto step = [&](int i, auto ph) {
         constexpr int P = decltype(ph)::value;

@@ -1,0 +1,95 @@
+"""The tiled kernel's copy waits, checked on the host against its issue order.
+
+The producer waves of the (BM x BN) tiled kernel issue LDS-direct copies that
+complete in issue order and wait on them with vmcnt(c), i.e. until at most c of
+their own copies are still in flight.  This test replays the issue order (the
+prologue's activation and weight copies, then per step the activation copy of
+step i+NA-1 and the weight copy of step i+PD) and checks that every wait the
+kernel takes guarantees the copies the next step reads: all prologue copies
+before the first expansion, the weights of step 1 before step 0, and at the
+end of step i the activation tile of step i+1 and the packed weights of step
+i+2.  The wait expressions are read from the kernel source, so an edit to them
+is checked here.
+"""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "nf4_bit_weight_amd", "csrc", "nf4_gemm.hip")
+
+
+def _expr(text, pattern):
+    m = re.search(pattern, text, re.S)
+    assert m, pattern
+    e = m.group(1)
+    # the only conditional form used: (a > b ? c : d)
+    e = re.sub(r"\(([^()?]+)\?([^():]+):([^()]+)\)", r"((\2) if (\1) else (\3))", e)
+    return e
+
+
+def _wait_exprs():
+    s = open(SRC).read()
+    return {
+        "after_a": _expr(s, r"constexpr int kAfterA = ([^;]+);"),
+        "after_w": _expr(s, r"constexpr int kAfterW = ([^;]+);"),
+        "pro1": _expr(s, r"wait_vm\(ic<(\(PD - 1\) \* kW)>\{\}\);"),
+        "pro2": _expr(s, r"expand_into\(0, 0, 0\);.*?wait_vm\(ic<(.+?)>\{\}\);"),
+    } if "expand_into(0, 0, 0);" in s else None
+
+
+def _replay(NA, PD, kA, kW, n, ex):
+    env = {"NA": NA, "PD": PD, "kA": kA, "kW": kW}
+    k_wait = min(eval(ex["after_a"], {}, env), eval(ex["after_w"], {}, env))
+    ops = []
+    done = 0                                   # ops[:done] known complete
+
+    def issue(kind, step, count):
+        ops.extend([(kind, step)] * count)
+
+    def wait(c):
+        nonlocal done
+        done = max(done, len(ops) - c)
+
+    def landed(kind, step):
+        return max(k for k, o in enumerate(ops) if o == (kind, step)) < done
+
+    for j in range(NA - 1):
+        issue("A", j, kA)
+    for j in range(PD):
+        issue("W", j, kW)
+    wait(eval(ex["pro1"], {}, env))
+    assert all(landed("A", j) for j in range(NA - 1)) and landed("W", 0), "prologue"
+    wait(eval(ex["pro2"], {}, env))
+    if n > 1:
+        assert landed("W", 1), "weights of step 1 before step 0"
+    for i in range(n):
+        issue("A", i + NA - 1, kA)
+        issue("W", i + PD, kW)
+        wait(k_wait)
+        if i + 1 < n:
+            assert landed("A", i + 1), f"end of step {i}: activation tile of step {i + 1}"
+        if i + 2 < n:
+            assert landed("W", i + 2), f"end of step {i}: weights of step {i + 2}"
+
+
+@pytest.mark.parametrize("NA,PD", [(4, 4), (2, 4), (2, 2)])
+def test_copy_waits_cover_every_read(NA, PD):
+    ex = _wait_exprs()
+    assert ex is not None, "prologue not found in the kernel source"
+    for kA in (1, 2, 4, 8, 16):               # activation copy instructions per wave
+        for kW in (3, 4):                     # weight copy instructions (plain, nested)
+            for n in range(1, 14):
+                _replay(NA, PD, kA, kW, n, ex)
+
+
+def test_replay_catches_the_steady_state_wait_in_the_prologue():
+    """The first step of four-deep rings needs the prologue's stricter wait:
+    with the weights of step 1 as the prologue's only requirement, the end of
+    step 0 leaves part of the weight copy of step 2 in flight."""
+    ex = dict(_wait_exprs())
+    ex["pro2"] = "(PD - 2) * kW"
+    with pytest.raises(AssertionError, match="weights of step 2"):
+        _replay(4, 4, 2, 3, 4, ex)

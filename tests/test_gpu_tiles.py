@@ -115,3 +115,47 @@ def test_register_operand_forward_repeats_bitwise(bn, plan_override):
     xb = WL.bf16_bits(x)
     assert_close(y0[:, torch.from_numpy(cols).to(DEV)], O.matmul_fwd(xb, wb), "sampled",
                  O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+
+
+# Tiles served by the producer / consumer kernel.  Its copy rings (2 or 4
+# activation stages, 2 or 4 packed-weight slots, by tile and direction) repeat
+# with a period of 4 steps, and its step loop is unrolled by 4.
+RING_TILES = [(256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1), (128, 128, 1), (64, 128, 1)]
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 10, 11, 13])
+@pytest.mark.parametrize("bm,bn,consumers", RING_TILES)
+def test_tiled_step_counts(steps, bm, bn, consumers, plan_override):
+    """One workgroup's contraction of 1 to 13 steps in both directions: every
+    remainder of the unrolled step loop with and without a whole period, and
+    fewer steps than the copy rings hold; the last step is ragged where the
+    step is deeper than one 64-block."""
+    plan_override(bm, bn, consumers, 1)
+    bk = 16384 // bn                                  # contraction depth of one step
+    M, nested = 96, steps % 2 == 1
+    seed = 700 + 16 * steps + bm // 64 + bn // 128 + consumers
+    # forward: the contraction runs over K
+    N, K = 136, steps * bk - (64 if bk == 128 else 0)
+    w = WL.weight_f32(N, K, WL.W_TINY, seed)
+    ref = O.quantize_nf4(w, nested=nested)
+    wq, wb = upload(ref, N, K, nested), ref_bits(ref, (N, K))
+    x = WL.x_bf16(M, K, WL.W_TINY, seed + 1)
+    xb = WL.bf16_bits(x)
+    api.nf4_reset_path_counts()
+    y = api.nf4_matmul_fwd(x.to(DEV), wq)
+    torch.cuda.synchronize()
+    c = api.nf4_path_counts()
+    assert c["fwd_tiled"] == 1 and c["splitk_reduce"] == 0
+    assert_close(y, O.matmul_fwd(xb, wb), f"y steps={steps}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+    # input gradient: the contraction runs over N
+    N, K = steps * bk - 8, 192
+    w = WL.weight_f32(N, K, WL.W_TINY, seed + 2)
+    ref = O.quantize_nf4(w, nested=nested)
+    wq, wb = upload(ref, N, K, nested), ref_bits(ref, (N, K))
+    gy = WL.grad_y_bf16(M, N, WL.W_TINY, seed + 3)
+    gyb = WL.bf16_bits(gy)
+    gx = api.nf4_matmul_bwd_input(gy.to(DEV), wq)
+    gx2 = api.nf4_matmul_bwd_input(gy.to(DEV), wq)
+    assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16)), "not bitwise repeatable"
+    assert_close(gx, O.matmul_bwd_input(gyb, wb), f"grad_x steps={steps}",
+                 O.matmul_bwd_input(abs_bits(gyb), abs_bits(wb)), N)
