@@ -1,4 +1,7 @@
-"""The tiled kernel's copy waits, checked on the host against its issue order.
+"""Copy waits of the two kernels that count their own copies, checked on the
+host against their issue order (the ping-pong input gradient waits for all of
+its copies every step, and the streaming kernel leaves its waits to the
+compiler).
 
 The producer waves of the (BM x BN) tiled kernel issue LDS-direct copies that
 complete in issue order and wait on them with vmcnt(c), i.e. until at most c of
@@ -93,3 +96,68 @@ def test_replay_catches_the_steady_state_wait_in_the_prologue():
     ex["pro2"] = "(PD - 2) * kW"
     with pytest.raises(AssertionError, match="weights of step 2"):
         _replay(4, 4, 2, 3, 4, ex)
+
+
+# ---- the register-operand forward kernel -------------------------------------------
+# Its producer work is done by every wave: per step i it issues the activation
+# copy of step i+2 and then the weight copy of step i+3 (into a 3-slot ring),
+# after a prologue W0 A0 W1 A1 W2.  Step i expands the weights of step i+1 and
+# ends with every wave's part of A(i+1) landed.
+
+def _rb_exprs():
+    s = open(SRC).read()
+    body = s[s.index("void k_rb("):]
+    return {
+        "kcopies": _expr(body, r"constexpr int kCopies = ([^;]+);"),
+        "pro_w0": _expr(body, r"wait_vm\(ic<([^>]+)>\{\}\);\s*// weights of step 0 landed"),
+        "pro_a0": _expr(body, r"wait_vm\(ic<([^>]+)>\{\}\);\s*// own part of A\(0\) landed"),
+        "step_w": _expr(body, r"wait_vm\(ic<([^>]+)>\{\}\);\s*// weights of step i\+1 landed"),
+        "step_a": _expr(body, r"may still be in flight\s*wait_vm\(ic<([^>]+)>\{\}\);"),
+    }
+
+
+def _replay_rb(kAJ, kWCopies, n, ex):
+    env = {"kAJ": kAJ, "kWCopies": kWCopies}
+    env["kCopies"] = eval(ex["kcopies"], {}, env)
+    ops, done = [], 0
+
+    def issue(kind, step, count):
+        ops.extend([(kind, step)] * count)
+
+    def wait(key):
+        nonlocal done
+        done = max(done, len(ops) - eval(ex[key], {}, env))
+
+    def landed(kind, step):
+        return max(k for k, o in enumerate(ops) if o == (kind, step)) < done
+
+    for kind, j in (("W", 0), ("A", 0), ("W", 1), ("A", 1), ("W", 2)):
+        issue(kind, j, kAJ if kind == "A" else kWCopies)
+    wait("pro_w0")
+    assert landed("W", 0), "prologue: weights of step 0"
+    wait("pro_a0")
+    assert landed("A", 0), "prologue: activation tile of step 0"
+    for i in range(n):
+        issue("A", i + 2, kAJ)
+        issue("W", i + 3, kWCopies)
+        wait("step_w")
+        if i + 1 < n:
+            assert landed("W", i + 1), f"step {i}: weights of step {i + 1}"
+        wait("step_a")
+        if i + 1 < n:
+            assert landed("A", i + 1), f"end of step {i}: activation tile of step {i + 1}"
+
+
+def test_register_operand_copy_waits_cover_every_read():
+    ex = _rb_exprs()
+    for kAJ in (1, 2, 4, 8):
+        for kWCopies in (2, 3):
+            for n in range(1, 10):
+                _replay_rb(kAJ, kWCopies, n, ex)
+
+
+def test_register_operand_replay_catches_a_short_wait():
+    ex = dict(_rb_exprs())
+    ex["step_a"] = "kCopies + kWCopies + 1"
+    with pytest.raises(AssertionError, match="activation tile"):
+        _replay_rb(2, 3, 4, ex)
