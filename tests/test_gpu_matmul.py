@@ -183,6 +183,6 @@ def test_llama_projection_m512(idx):
     _full_size(WL.LLAMA_8B, idx, WL.LLAMA_M, WL.W_LLAMA)
 
 
-@pytest.mark.parametrize("idx", [0, 1, 6])
+@pytest.mark.parametrize("idx", [0, 1, 4, 6])          # q/o, k/v, gate/up, down: each distinct shape
 def test_qwen_projection_m2048(idx):
     _full_size(WL.QWEN_32B, idx, WL.QWEN_M, WL.W_QWEN, sample_rows=32)

@@ -100,7 +100,7 @@ def test_small_m_matches_tiled_and_repeats():
 
 
 @pytest.mark.parametrize("M", list(WL.DECODE_MS))
-@pytest.mark.parametrize("idx", [1, 4, 6])       # k (N = 1024), gate (14336), down (K = 14336)
+@pytest.mark.parametrize("idx", [0, 1, 4, 6])    # q/o (4096), k/v (N = 1024), gate/up (14336), down (K = 14336)
 def test_llama_decode_shapes(M, idx):
     p = WL.LLAMA_8B[idx]
     w = WL.weight_f32(p.N, p.K, WL.W_LLAMA, 0, idx)
