@@ -1601,7 +1601,7 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   return pl;
 }
 
-GemmPlan plan_grouped(GemmKind, int64_t total_M, int64_t, int64_t, int32_t E) {
+GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int32_t E) {
   GemmPlan pl{};
   pl.small_m = false;
   pl.splits = 1;
@@ -1611,6 +1611,35 @@ GemmPlan plan_grouped(GemmKind, int64_t total_M, int64_t, int64_t, int32_t E) {
   const int64_t mean = (E > 0) ? (total_M + E - 1) / E : total_M;
   pl.bm = (mean <= 96) ? 64 : (mean <= 192 ? 128 : 256);
   pl.consumers = (pl.bm == 256) ? 0 : 1;
+  if (mean <= 96) {
+    // Few rows per expert.  A 256-row tile leaves most of its rows empty, but
+    // it expands each weight tile once per expert (a 64-row tile expands it
+    // twice for the experts just over 64 rows) and the 256-row kernels run
+    // faster per step.  Measured on MI355X with 64 experts of 46-86 rows
+    // (OLMoE shapes): the register-operand forward at 256 x 128 for N = 1024
+    // and 256 x 256 for N = 2048 (-3..6% and -22% against 64 x 256); the
+    // ping-pong input gradient for 2048 output columns (-5%), while 64 x 256
+    // stays best for 1024.
+    if (kind == GemmKind::kFwd) {
+      pl.bm = 256;
+      pl.bn = (N >= 2048) ? 256 : 128;
+      pl.consumers = 3;
+    } else if (K >= 2048) {
+      pl.bm = 256;
+      pl.bn = 256;
+      pl.consumers = 0;
+    }
+  }
+  // Tuning overrides (documented): NF4_BM, NF4_BN, NF4_CONSUMERS select the
+  // tile as for a single product; there is no split of the contraction here.
+  const int o_bm = env_int("NF4_BM"), o_bn = env_int("NF4_BN"), o_c = env_int("NF4_CONSUMERS");
+  if (o_bm != 0 || o_bn != 0 || o_c != 0) {
+    if (o_bm == 64 || o_bm == 128 || o_bm == 256) pl.bm = o_bm;
+    if (o_bn == 128 || o_bn == 256) pl.bn = o_bn;
+    if (pl.bm == 256 && !(kind == GemmKind::kFwd && o_bn == 128 && o_c != 2 && o_c != 4)) pl.bn = 256;
+    pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
+    if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
+  }
   return pl;
 }
 

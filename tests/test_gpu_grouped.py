@@ -1,5 +1,7 @@
 """GPU parity of the grouped (expert) forward and input gradient."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -76,3 +78,44 @@ def test_olmoe_experts(proj):
                  O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)
     y2 = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("bm,bn,consumers", [(64, 256, 1), (64, 128, 1), (128, 256, 1), (128, 256, 2),
+                                             (128, 128, 1), (256, 256, 4), (256, 256, 0), (256, 128, 0)])
+def test_grouped_tiles(bm, bn, consumers):
+    """Every tile the grouped products can be given through NF4_BM / NF4_BN /
+    NF4_CONSUMERS, on ragged experts (empty ones, one spanning two 128-row
+    tiles): 256 x 256 is the ping-pong kernel in both directions with
+    consumers 4 and the register-operand forward with 0, 256 x 128 the
+    4-wave register-operand forward."""
+    E, N, K = 6, 136, 192
+    counts = np.array([3, 0, 70, 129, 0, 1])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(offsets[-1])
+    wq, wb = _stack(E, N, K, True, 9)
+    x = WL.x_bf16(T, K, WL.W_OLMOE, 90)
+    gy = WL.grad_y_bf16(T, N, WL.W_OLMOE, 91)
+    off = torch.from_numpy(offsets).to(DEV)
+    keys = ("NF4_BM", "NF4_BN", "NF4_CONSUMERS")
+    saved = {k: os.environ.get(k) for k in keys}
+    os.environ.update({"NF4_BM": str(bm), "NF4_BN": str(bn), "NF4_CONSUMERS": str(consumers)})
+    try:
+        api.nf4_reset_path_counts()
+        y = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+        gx = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
+        y2 = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+        torch.cuda.synchronize()
+        c = api.nf4_path_counts()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert c["grouped_fwd"] == 2 and c["grouped_bwd"] == 1
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not bitwise repeatable"
+    xb, gyb, aw = WL.bf16_bits(x), WL.bf16_bits(gy), abs_bits(wb)
+    assert_close(y, O.grouped_matmul_fwd(xb, offsets, wb), "grouped y",
+                 O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
+    assert_close(gx, O.grouped_matmul_bwd_input(gyb, offsets, wb), "grouped grad_x",
+                 O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)
