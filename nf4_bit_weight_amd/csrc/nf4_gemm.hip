@@ -1524,8 +1524,12 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // rows), mid-size ones 128 x 128 (4x the tiles), small ones 64 x 128.
   const double macs = static_cast<double>(M) * static_cast<double>(nc) * static_cast<double>(kc);
   // The forward takes the register-operand kernel from 4e9 MACs at M > 128
-  // (tile width and split chosen by the cost model below).
-  if ((macs >= 2e10 || (kind == GemmKind::kFwd && macs >= 4e9)) && M > 128) {
+  // (tile width and split chosen by the cost model below); so does the input
+  // gradient (ping-pong kernel) once its 256 x 256 tiles alone fill half the
+  // compute units (Qwen k/v at M = 2048: 160 tiles, 43 vs 57 us with
+  // 128 x 128; the M = 512 q/o input gradients, 32 tiles, stay at 128 x 128).
+  const int64_t tiles256 = ((M + 255) / 256) * ((nc + 255) / 256);
+  if ((macs >= 2e10 || (macs >= 4e9 && (kind == GemmKind::kFwd || 2 * tiles256 >= cus))) && M > 128) {
     pl.bm = 256; pl.bn = 256;
   } else if (macs >= 4e9 && M > 64) {
     pl.bm = 128; pl.bn = 128;
