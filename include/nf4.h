@@ -60,9 +60,14 @@
  *   Empty      M == 0 (or N*K == 0 for the codec) returns NF4_OK with no work;
  *              the activation and output pointers may then be NULL.
  *   Determinism  Every kernel sums in a fixed order and uses no atomics; the
- *              split of a contraction across workgroups is a pure function of
- *              (M, N, K, compute-unit count).  Repeated calls with the same
- *              inputs give bitwise identical outputs.
+ *              tile and the split of a contraction across workgroups are a
+ *              pure function of (M, N, K, compute-unit count), for the grouped
+ *              calls of (total_M, E, N, K), and of the NF4_BM, NF4_BN,
+ *              NF4_CONSUMERS, NF4_SPLITS, NF4_SMALL_M and NF4_GEMV_* tuning
+ *              variables when they are set (read on every call; a different
+ *              tile may round differently in the last bit).  Repeated calls
+ *              with the same inputs and environment give bitwise identical
+ *              outputs.
  */
 #ifndef NF4_H_
 #define NF4_H_
