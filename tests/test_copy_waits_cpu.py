@@ -45,7 +45,7 @@ def _wait_exprs():
 
 def _replay(NA, PD, kA, kW, n, ex):
     env = {"NA": NA, "PD": PD, "kA": kA, "kW": kW}
-    k_wait = min(eval(ex["after_a"], {}, env), eval(ex["after_w"], {}, env))
+    k_wait = min(eval(ex["after_a"], {"__builtins__": {}}, env), eval(ex["after_w"], {"__builtins__": {}}, env))
     ops = []
     done = 0                                   # ops[:done] known complete
 
@@ -63,9 +63,9 @@ def _replay(NA, PD, kA, kW, n, ex):
         issue("A", j, kA)
     for j in range(PD):
         issue("W", j, kW)
-    wait(eval(ex["pro1"], {}, env))
+    wait(eval(ex["pro1"], {"__builtins__": {}}, env))
     assert all(landed("A", j) for j in range(NA - 1)) and landed("W", 0), "prologue"
-    wait(eval(ex["pro2"], {}, env))
+    wait(eval(ex["pro2"], {"__builtins__": {}}, env))
     if n > 1:
         assert landed("W", 1), "weights of step 1 before step 0"
     for i in range(n):
@@ -118,7 +118,7 @@ def _rb_exprs():
 
 def _replay_rb(kAJ, kWCopies, n, ex):
     env = {"kAJ": kAJ, "kWCopies": kWCopies}
-    env["kCopies"] = eval(ex["kcopies"], {}, env)
+    env["kCopies"] = eval(ex["kcopies"], {"__builtins__": {}}, env)
     ops, done = [], 0
 
     def issue(kind, step, count):
@@ -126,7 +126,7 @@ def _replay_rb(kAJ, kWCopies, n, ex):
 
     def wait(key):
         nonlocal done
-        done = max(done, len(ops) - eval(ex[key], {}, env))
+        done = max(done, len(ops) - eval(ex[key], {"__builtins__": {}}, env))
 
     def landed(kind, step):
         return max(k for k, o in enumerate(ops) if o == (kind, step)) < done
