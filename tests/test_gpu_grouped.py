@@ -57,6 +57,27 @@ def test_grouped_identity_rows():
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("nested", [False, True])
+def test_grouped_transposed_identity_rows(nested):
+    """Each routed row of grad_y is a unit vector e_j: the input gradient's row
+    is row j of W_hat_e, bit for bit (the transposed read of the same packed
+    stack)."""
+    E, N, K = 5, 72, 192
+    wq, wb = _stack(E, N, K, nested, 16)
+    counts = np.array([7, 0, 3, 12, 1])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(offsets[-1])
+    j = np.random.default_rng(4).integers(0, N, size=T)
+    gy = torch.zeros((T, N), dtype=torch.bfloat16)
+    gy[np.arange(T), j] = 1.0
+    off = torch.from_numpy(offsets).to(DEV)
+    gx = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
+    got = gx.cpu().view(torch.int16).numpy().view(np.uint16)
+    exp = np.repeat(np.arange(E), counts)
+    want = np.stack([wb[exp[t], j[t], :] for t in range(T)])
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("proj", ["gate", "down"])
 def test_olmoe_experts(proj):
     """OLMoE-1B-7B experts: 512 tokens, top-8 of 64, nested NF4 stacks."""
@@ -76,8 +97,14 @@ def test_olmoe_experts(proj):
                  O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
     assert_close(gx, O.grouped_matmul_bwd_input(gyb, offsets, wb), f"olmoe {proj} gx",
                  O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)
+    # bitwise run-to-run repeat of both directions, the second run after an
+    # unrelated launch of the other direction on other inputs
+    api.nf4_grouped_matmul_fwd(torch.flip(x, [0]).to(DEV), off, wq, E)
+    gx2 = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
+    api.nf4_grouped_matmul_bwd_input(torch.flip(gy, [0]).to(DEV), off, wq, E)
     y2 = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16))
 
 
 @pytest.mark.parametrize("bm,bn,consumers", [(64, 256, 1), (64, 128, 1), (128, 256, 1), (128, 256, 2),
@@ -104,6 +131,7 @@ def test_grouped_tiles(bm, bn, consumers):
         y = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
         gx = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
         y2 = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+        gx2 = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
         torch.cuda.synchronize()
         c = api.nf4_path_counts()
     finally:
@@ -112,8 +140,9 @@ def test_grouped_tiles(bm, bn, consumers):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    assert c["grouped_fwd"] == 2 and c["grouped_bwd"] == 1
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not bitwise repeatable"
+    assert c["grouped_fwd"] == 2 and c["grouped_bwd"] == 2
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "forward not bitwise repeatable"
+    assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16)), "input gradient not bitwise repeatable"
     xb, gyb, aw = WL.bf16_bits(x), WL.bf16_bits(gy), abs_bits(wb)
     assert_close(y, O.grouped_matmul_fwd(xb, offsets, wb), "grouped y",
                  O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
