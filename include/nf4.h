@@ -57,8 +57,12 @@
  *              negative NF4_ERR_* code.  On error nothing is enqueued and no
  *              output is touched.  nf4_status_str() names each code.  No C++
  *              exception crosses this interface.
- *   Empty      M == 0 (or N*K == 0 for the codec) returns NF4_OK with no work;
- *              the activation and output pointers may then be NULL.
+ *   Empty      M == 0 (or N*K == 0 for the codec) returns NF4_OK with no work.
+ *              A product whose contraction is empty (forward K == 0, input
+ *              gradient N == 0) writes zeros with a fill kernel (never a
+ *              memset, so the call can be captured into a HIP graph).  An
+ *              operand with no elements may be NULL (as torch gives for empty
+ *              tensors).
  *   Determinism  Every kernel sums in a fixed order and uses no atomics; the
  *              tile and the split of a contraction across workgroups are a
  *              pure function of (M, N, K, compute-unit count), for the grouped

@@ -11,8 +11,13 @@ through save_for_backward, and the saved tensors carry autograd's version
 counter, so an in-place change of a saved weight between forward and backward
 raises instead of silently producing wrong gradients.
 
-Only integers (N, K, E) live on ctx.  The weight is frozen: no gradient is
-returned for any weight field.
+Only integers (N, K, E) and the caller's dtype live on ctx.  The weight is
+frozen: no gradient is returned for any weight field.
+
+dtype handling follows Linear4bit's forward (Soup issue #842, "Design
+sketch": the Function keeps its dtype behaviour): the kernels compute in bf16
+with fp32 accumulation, and the output (and the input gradient) come back in
+the dtype the caller passed in.
 """
 
 from __future__ import annotations
@@ -41,7 +46,8 @@ class NF4MatMul(torch.autograd.Function):
         y = api.nf4_matmul_fwd(x2.contiguous(), w)
         ctx.save_for_backward(packed, absmax, nested_absmax, nested_offset, code, nested_code)
         ctx.N, ctx.K = int(N), int(K)
-        return y.reshape(*lead, N)
+        ctx.x_dtype = x.dtype
+        return y.reshape(*lead, N).to(x.dtype)
 
     @staticmethod
     def backward(ctx, grad_y):
@@ -53,6 +59,7 @@ class NF4MatMul(torch.autograd.Function):
             if g2.dtype != torch.bfloat16:
                 g2 = g2.to(torch.bfloat16)
             grad_x = api.nf4_matmul_bwd_input(g2.contiguous(), w).reshape(*lead, ctx.K)
+            grad_x = grad_x.to(ctx.x_dtype)
         return grad_x, None, None, None, None, None, None, None, None
 
 
@@ -69,7 +76,8 @@ class NF4GroupedMatMul(torch.autograd.Function):
         ctx.save_for_backward(offsets, packed, absmax, nested_absmax, nested_offset, code,
                               nested_code)
         ctx.E, ctx.N, ctx.K = int(E), int(N), int(K)
-        return y
+        ctx.x_dtype = x.dtype
+        return y.to(x.dtype)
 
     @staticmethod
     def backward(ctx, grad_y):
@@ -79,6 +87,7 @@ class NF4GroupedMatMul(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             g = grad_y if grad_y.dtype == torch.bfloat16 else grad_y.to(torch.bfloat16)
             grad_x = api.nf4_grouped_matmul_bwd_input(g.contiguous(), offsets, w, ctx.E)
+            grad_x = grad_x.to(ctx.x_dtype)
         return (grad_x,) + (None,) * 10
 
 

@@ -25,10 +25,11 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int check_w(const uint8_t* packed, const void* absmax, const float* nested_absmax,
             const float* nested_offset, const float* code16, const float* ncode, int64_t N,
             int64_t K) {
-  if (!packed || !absmax || !code16) return NF4_ERR_NULL;
-  if (nested_absmax && (!nested_offset || !ncode)) return NF4_ERR_NULL;
   if (N < 0 || K < 0) return NF4_ERR_SHAPE;
   if (N > 0 && K > INT64_MAX / N) return NF4_ERR_SHAPE;
+  // a weight with no elements has no packed bytes or scales to point at
+  if (!code16 || ((!packed || !absmax) && N * K != 0)) return NF4_ERR_NULL;
+  if (nested_absmax && (!nested_offset || !ncode)) return NF4_ERR_NULL;
   if ((N * K) % 2) return NF4_ERR_SHAPE;
   if (!aligned16(packed)) return NF4_ERR_ALIGN;
   return NF4_OK;
@@ -44,6 +45,24 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K, bool bwd) {
 
 int to_status(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 
+// Zero fill of a bf16 output whose contraction is empty.  A kernel rather than
+// hipMemsetAsync, so that a caller capturing the call into a HIP graph records
+// a kernel node and never a memset node.  `out` is 16-byte aligned.
+__global__ __launch_bounds__(256) void k_zero_bf16(uint16_t* __restrict__ out, int64_t n) {
+  const int64_t n8 = n / 8;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8; i += stride)
+    reinterpret_cast<uint4*>(out)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x == 0 && threadIdx.x < n - 8 * n8) out[8 * n8 + threadIdx.x] = 0;
+}
+
+hipError_t zero_bf16(void* out, int64_t n, hipStream_t stream) {
+  const int64_t blocks = (n / 8 + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks));
+  k_zero_bf16<<<grid, 256, 0, stream>>>(static_cast<uint16_t*>(out), n);
+  return hipGetLastError();
+}
+
 int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed,
                   const void* absmax, const float* nested_absmax, const float* nested_offset,
                   const float* code16, const float* ncode, int64_t N, int64_t K, void* C,
@@ -51,17 +70,18 @@ int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed
   const bool bwd = kind == GemmKind::kBwdInput;
   int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K);
   if (st) return st;
-  // an empty batch reads and writes nothing: its activation and output may be NULL
-  // (as torch gives for empty tensors)
-  if ((!A || !C) && M != 0) return NF4_ERR_NULL;
+  // an operand with no elements (empty batch, empty contraction, no output
+  // columns) is never read or written and may be NULL, as torch gives for
+  // empty tensors
+  if (!A && M != 0 && (bwd ? N : K) != 0) return NF4_ERR_NULL;
+  if (!C && M != 0 && (bwd ? K : N) != 0) return NF4_ERR_NULL;
   st = check_gemm_shape(M, N, K, bwd);
   if (st) return st;
   if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
   if (M == 0 || N == 0 || K == 0) {
     if (M > 0 && (bwd ? K : N) > 0) {
       // an empty contraction: the product is all zeros
-      const size_t bytes = static_cast<size_t>(M) * static_cast<size_t>(bwd ? K : N) * 2;
-      return to_status(hipMemsetAsync(C, 0, bytes, static_cast<hipStream_t>(stream)));
+      return to_status(zero_bf16(C, M * (bwd ? K : N), static_cast<hipStream_t>(stream)));
     }
     return NF4_OK;
   }
@@ -85,14 +105,15 @@ int grouped_common(GemmKind kind, const void* A, const int32_t* offsets, int32_t
   int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode,
                    static_cast<int64_t>(E) * N, K);
   if (st) return st;
-  if (!offsets || ((!A || !C) && total_M != 0)) return NF4_ERR_NULL;
+  if (!offsets) return NF4_ERR_NULL;
+  if (!A && total_M != 0 && (bwd ? N : K) != 0) return NF4_ERR_NULL;
+  if (!C && total_M != 0 && (bwd ? K : N) != 0) return NF4_ERR_NULL;
   st = check_gemm_shape(total_M, N, K, bwd);
   if (st) return st;
   if (!aligned16(A) || !aligned16(C)) return NF4_ERR_ALIGN;
   if (total_M == 0 || N == 0 || K == 0) {
     if (total_M > 0 && (bwd ? K : N) > 0) {
-      const size_t bytes = static_cast<size_t>(total_M) * static_cast<size_t>(bwd ? K : N) * 2;
-      return to_status(hipMemsetAsync(C, 0, bytes, static_cast<hipStream_t>(stream)));
+      return to_status(zero_bf16(C, total_M * (bwd ? K : N), static_cast<hipStream_t>(stream)));
     }
     return NF4_OK;
   }

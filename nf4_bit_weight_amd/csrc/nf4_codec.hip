@@ -70,25 +70,50 @@ __global__ __launch_bounds__(kThreads) void k_quant_blocks(const T* __restrict__
   if ((g & 7) == 0) absmax_out[g >> 3] = m;
 }
 
-// Nested step 1: fp64 sequential sum of each chunk of 256 absmax values.
+// Nested step 1: fp64 sequential sum of each chunk of 256 absmax values.  One
+// wave per chunk: the wave reads the chunk with coalesced 16-byte loads into
+// its LDS slice, then lane 0 adds the 256 values in index order (the order the
+// mean offset is defined with, so it is reproduced bit for bit).
+constexpr int kSumWaves = kThreads / 64;
 __global__ __launch_bounds__(kThreads) void k_chunk_sums(const float* __restrict__ absmax,
                                                          int64_t nb, double* __restrict__ sums) {
-  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  __shared__ float chunk[kSumWaves][kNestedBlock];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kSumWaves + wave;
   const int64_t b0 = g * kNestedBlock;
-  if (b0 >= nb) return;
-  const int64_t b1 = (b0 + kNestedBlock < nb) ? b0 + kNestedBlock : nb;
+  if (b0 >= nb) return;                                   // whole wave leaves together
+  const int64_t len = (b0 + kNestedBlock < nb) ? kNestedBlock : nb - b0;
+  if (len == kNestedBlock && (reinterpret_cast<uintptr_t>(absmax) & 15u) == 0) {
+    reinterpret_cast<f32x4_t*>(chunk[wave])[lane] = reinterpret_cast<const f32x4_t*>(absmax + b0)[lane];
+  } else {
+    for (int i = lane; i < len; i += 64) chunk[wave][i] = absmax[b0 + i];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane != 0) return;
   double s = 0.0;
-  for (int64_t b = b0; b < b1; ++b) s += static_cast<double>(absmax[b]);
+  for (int i = 0; i < len; ++i) s += static_cast<double>(chunk[wave][i]);
   sums[g] = s;
 }
 
-// Nested step 2: one thread sums the chunk sums in order and writes the offset.
-__global__ void k_offset(const double* __restrict__ sums, int64_t ng, int64_t nb,
-                         float* __restrict__ offset) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// Nested step 2: the chunk sums are added in order g = 0, 1, ... by one thread;
+// the workgroup stages them through LDS in coalesced pieces so the serial
+// chain waits on LDS, not on a global load per term.
+constexpr int kOffPiece = 2048;
+__global__ __launch_bounds__(kThreads) void k_offset(const double* __restrict__ sums, int64_t ng,
+                                                     int64_t nb, float* __restrict__ offset) {
+  __shared__ double piece[kOffPiece];
   double s = 0.0;
-  for (int64_t g = 0; g < ng; ++g) s += sums[g];
-  offset[0] = static_cast<float>(s / static_cast<double>(nb));
+  for (int64_t g0 = 0; g0 < ng; g0 += kOffPiece) {
+    const int len = static_cast<int>(ng - g0 < kOffPiece ? ng - g0 : kOffPiece);
+    for (int i = threadIdx.x; i < len; i += kThreads) piece[i] = sums[g0 + i];
+    __syncthreads();
+    if (threadIdx.x == 0)
+      for (int i = 0; i < len; ++i) s += piece[i];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) offset[0] = static_cast<float>(s / static_cast<double>(nb));
 }
 
 // Nested step 3: one workgroup per group of 256 absmax values.
@@ -228,8 +253,9 @@ hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, const float
   if (!nested) return hipGetLastError();
   double* sums = reinterpret_cast<double*>(static_cast<char*>(ws) +
                                            align_up(static_cast<size_t>(nb) * 4, 256));
-  k_chunk_sums<<<grid_for(ng), kThreads, 0, stream>>>(am32, nb, sums);
-  k_offset<<<1, 64, 0, stream>>>(sums, ng, nb, nested_offset);
+  k_chunk_sums<<<static_cast<unsigned>((ng + kSumWaves - 1) / kSumWaves), kThreads, 0, stream>>>(
+      am32, nb, sums);
+  k_offset<<<1, kThreads, 0, stream>>>(sums, ng, nb, nested_offset);
   k_nested<<<static_cast<unsigned>(ng), kThreads, 0, stream>>>(
       am32, nb, ncode, nested_offset, static_cast<uint8_t*>(absmax), nested_absmax);
   return hipGetLastError();

@@ -141,6 +141,40 @@ __device__ __forceinline__ int xcd_tile(int L, int T) {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
+// Rows of row tile mt: [row0, row_end) of A and C, and the first row of the
+// weight tensor it multiplies.  Dense: tile mt of BM rows.  Grouped: the row
+// tiles are numbered expert by expert (ceil(rows_e / BM) tiles each, from the
+// expert-sorted offsets[E + 1], every entry clamped into [0, M] so a malformed
+// array cannot index out of range); the tile stops at its expert's last row
+// and meets that expert's slice of the [E * N, K] stack.  Returns false for a
+// tile id past the last expert's tiles (m_tiles is an upper bound).
+template <int BM, bool GROUPED>
+__device__ __forceinline__ bool row_tile(const GemmParams& p, int mt, int64_t N, int64_t& row0,
+                                         int64_t& row_end, int64_t& wrow_base) {
+  if constexpr (GROUPED) {
+    int acc = 0;
+    for (int e = 0; e < p.E; ++e) {
+      int64_t a = p.offsets[e], b = p.offsets[e + 1];
+      a = a < 0 ? 0 : (a > p.M ? p.M : a);
+      b = b < a ? a : (b > p.M ? p.M : b);
+      const int cnt = static_cast<int>((b - a + BM - 1) / BM);
+      if (mt < acc + cnt) {
+        row0 = a + static_cast<int64_t>(mt - acc) * BM;
+        row_end = b;
+        wrow_base = static_cast<int64_t>(e) * N;
+        return true;
+      }
+      acc += cnt;
+    }
+    return false;
+  } else {
+    row0 = static_cast<int64_t>(mt) * BM;
+    row_end = p.M;
+    wrow_base = 0;
+    return true;
+  }
+}
+
 template <int BM, int BN, bool TRANS, bool NESTED, bool GROUPED, int C>
 __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
   using T = Tile<BM, BN, TRANS, C>;
@@ -165,26 +199,8 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
   const int cz = t / p.m_tiles;
   const int z = cz % p.splits;
   const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
-  int64_t row0, row_end, wrow_base = 0;
-  if constexpr (GROUPED) {
-    int acc = 0, e_found = -1;
-    int64_t lo = 0, hi = 0;
-    for (int e = 0; e < p.E; ++e) {
-      int64_t a = p.offsets[e], b = p.offsets[e + 1];
-      a = a < 0 ? 0 : (a > p.M ? p.M : a);
-      b = b < a ? a : (b > p.M ? p.M : b);
-      const int cnt = static_cast<int>((b - a + BM - 1) / BM);
-      if (mt < acc + cnt) { e_found = e; lo = a + static_cast<int64_t>(mt - acc) * BM; hi = b; break; }
-      acc += cnt;
-    }
-    if (e_found < 0) return;
-    row0 = lo;
-    row_end = hi;
-    wrow_base = static_cast<int64_t>(e_found) * N;
-  } else {
-    row0 = static_cast<int64_t>(mt) * BM;
-    row_end = p.M;
-  }
+  int64_t row0, row_end, wrow_base;
+  if (!row_tile<BM, GROUPED>(p, mt, N, row0, row_end, wrow_base)) return;
   const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
   const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
   const int n = ke - kb;                   // steps of this workgroup
@@ -643,26 +659,8 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   const int cz = tt / p.m_tiles;
   const int z = cz % p.splits;
   const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
-  int64_t row0, row_end, wrow_base = 0;
-  if constexpr (GROUPED) {
-    int acc = 0, e_found = -1;
-    int64_t lo = 0, hi = 0;
-    for (int e = 0; e < p.E; ++e) {
-      int64_t a = p.offsets[e], b = p.offsets[e + 1];
-      a = a < 0 ? 0 : (a > p.M ? p.M : a);
-      b = b < a ? a : (b > p.M ? p.M : b);
-      const int cnt = static_cast<int>((b - a + BM - 1) / BM);
-      if (mt < acc + cnt) { e_found = e; lo = a + static_cast<int64_t>(mt - acc) * BM; hi = b; break; }
-      acc += cnt;
-    }
-    if (e_found < 0) return;
-    row0 = lo;
-    row_end = hi;
-    wrow_base = static_cast<int64_t>(e_found) * N;
-  } else {
-    row0 = static_cast<int64_t>(mt) * BM;
-    row_end = p.M;
-  }
+  int64_t row0, row_end, wrow_base;
+  if (!row_tile<BM, GROUPED>(p, mt, N, row0, row_end, wrow_base)) return;
   const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
   const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
   const int n = ke - kb;
@@ -1092,26 +1090,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
   const int cz = tt / p.m_tiles;
   const int z = cz % p.splits;
   const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
-  int64_t row0, row_end, wrow_base = 0;
-  if constexpr (GROUPED) {
-    int acc = 0, e_found = -1;
-    int64_t lo = 0, hi = 0;
-    for (int e = 0; e < p.E; ++e) {
-      int64_t a = p.offsets[e], b = p.offsets[e + 1];
-      a = a < 0 ? 0 : (a > p.M ? p.M : a);
-      b = b < a ? a : (b > p.M ? p.M : b);
-      const int cnt = static_cast<int>((b - a + BM - 1) / BM);
-      if (mt < acc + cnt) { e_found = e; lo = a + static_cast<int64_t>(mt - acc) * BM; hi = b; break; }
-      acc += cnt;
-    }
-    if (e_found < 0) return;
-    row0 = lo;
-    row_end = hi;
-    wrow_base = static_cast<int64_t>(e_found) * N;
-  } else {
-    row0 = static_cast<int64_t>(mt) * BM;
-    row_end = p.M;
-  }
+  int64_t row0, row_end, wrow_base;
+  if (!row_tile<BM, GROUPED>(p, mt, N, row0, row_end, wrow_base)) return;
   const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
   const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
   const int n = ke - kb;

@@ -86,6 +86,10 @@ def test_matmul_validation(lib):
     assert _fwd(lib, M=0) == L.NF4_OK                         # empty: nothing to do
     assert _fwd(lib, M=0, x=None, y=None) == L.NF4_OK         # empty tensors may be NULL
     assert _fwd(lib, M=0, packed=None) == L.NF4_ERR_NULL      # the weight is still checked
+    # a weight with no elements (N = 0) has nothing to point at; the output
+    # has no columns, so nothing is launched
+    assert _fwd(lib, N=0, packed=None, absmax=None, y=None) == L.NF4_OK
+    assert _fwd(lib, N=0, packed=None, absmax=None, code=None) == L.NF4_ERR_NULL
     bw = lib.nf4_matmul_bwd_input(FAKE, 4, FAKE, FAKE, None, None, FAKE, None, 12, 64, FAKE,
                                   None, 0, None)
     assert bw == L.NF4_ERR_UNSUPPORTED                        # N % 8 for the input grad
@@ -148,3 +152,14 @@ def test_library_has_no_undefined_internal_symbols():
                          check=True).stdout
     bad = [ln for ln in out.splitlines() if "nf4" in ln]
     assert not bad, bad
+
+
+def test_no_memset_in_library_sources():
+    """The library zeroes with its own kernel, never hipMemset*: a caller may
+    capture any entry point into a HIP graph, and a captured memset node is
+    avoided on this target."""
+    csrc = os.path.join(ROOT, "nf4_bit_weight_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, name)).read()
+        code = re.sub(r"//[^\n]*", "", re.sub(r"/\*.*?\*/", "", text, flags=re.S))
+        assert not re.search(r"\bhipMemset\w*\s*\(", code), f"{name} calls hipMemset"

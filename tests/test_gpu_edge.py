@@ -76,3 +76,56 @@ def test_narrow_shapes(M, N, K, nested):
     assert_close(y, O.matmul_fwd(xb, wb), f"y {M}x{N}x{K}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
     assert_close(gx, O.matmul_bwd_input(gyb, wb), f"gx {M}x{N}x{K}",
                  O.matmul_bwd_input(abs_bits(gyb), abs_bits(wb)), N)
+
+
+@pytest.mark.parametrize("nested", [False, True])
+def test_empty_contraction_zero_fill(nested):
+    """N = 0 (forward) or K = 0 (input gradient) with rows present: the output
+    is all zeros, written by a fill kernel (replayed from a HIP graph too)."""
+    M, K = 37, 128
+    wq, _ = _weight(64, K, nested, 9)
+    w0 = api.NF4Weight(wq.packed[:0], wq.absmax[:0],
+                       wq.nested_absmax[:0] if nested else None, wq.nested_offset,
+                       wq.code, wq.nested_code, 0, K)
+    x = torch.randn((M, K), device=DEV).to(torch.bfloat16)
+    y = torch.full((M, 0), 1.0, dtype=torch.bfloat16, device=DEV)
+    assert tuple(api.nf4_matmul_fwd(x, w0, out=y).shape) == (M, 0)
+    gx = torch.full((M, K), 7.0, dtype=torch.bfloat16, device=DEV)
+    g = torch.empty((M, 0), dtype=torch.bfloat16, device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.nf4_matmul_bwd_input(g, w0, out=gx)
+    for _ in range(3):
+        gx.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(gx.float()) == 0
+    gx.fill_(7.0)
+    api.nf4_matmul_bwd_input(g, w0, out=gx)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gx.float()) == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16, torch.bfloat16])
+def test_autograd_keeps_caller_dtype(dtype):
+    """The wrapper computes in bf16 and hands back the caller's dtype, for the
+    output and for the input gradient (plain and grouped)."""
+    from nf4_bit_weight_amd.autograd import nf4_grouped_linear, nf4_linear
+    N, K, M = 128, 256, 16
+    wq, _ = _weight(N, K, True, 11)
+    x = torch.randn((M, K), device=DEV, dtype=dtype, requires_grad=True)
+    y = nf4_linear(x, wq)
+    assert y.dtype == dtype
+    y.float().sum().backward()
+    assert x.grad.dtype == dtype
+    ref = nf4_linear(x.detach().to(torch.bfloat16), wq)
+    assert torch.equal(y.to(torch.bfloat16).view(torch.int16), ref.view(torch.int16))
+    E = 2
+    wg, _ = _weight(E * N, K, True, 12)
+    off = torch.tensor([0, 5, M], dtype=torch.int32, device=DEV)
+    xg = torch.randn((M, K), device=DEV, dtype=dtype, requires_grad=True)
+    yg = nf4_grouped_linear(xg, off, wg.per_expert(E), E)
+    assert yg.dtype == dtype
+    yg.float().sum().backward()
+    assert xg.grad.dtype == dtype
