@@ -1,37 +1,38 @@
 """Weight-aliasing harness for the checkpoint-visible NF4 wrapper.
 
-bitsandbytes issue #2034 ("Minimal reproducer", "What it prints", "Root
-cause") and Soup issue #842 ("Acceptance criteria", aliasing control): a
-streaming caller copies each layer's packed weight into a small ring of
-recycled device buffers inside a non-reentrant ``torch.utils.checkpoint``
-region.  A wrapper that routes every weight field through
-``save_for_backward`` gets the recompute's freshly copied bytes in backward;
-a wrapper that keeps them on ctx as attributes reads whatever a later copy
-left in the slot, so its input gradients come out wrong while the forward
-stays bit-exact.
+What it checks comes from bitsandbytes issue #2034 ("Minimal reproducer",
+"What it prints", "Root cause") and Soup issue #842 ("Acceptance criteria",
+the aliasing control).  A streaming caller fills a small set of reused
+device slots with each layer's packed weight, and the fill happens inside a
+non-reentrant ``torch.utils.checkpoint`` region.  The recompute therefore
+fills a slot again, and that slot is not necessarily the one the original
+forward used.  A wrapper whose weight fields travel through
+``save_for_backward`` gets the recompute's bytes in its backward.  A wrapper
+that keeps them as ctx attributes reads whatever the slot holds by then.
+Its input gradients are wrong, while its forward is bit-exact.
 
-Arms (each run twice, with recycled slots and with a private buffer per
-layer, then compared gradient by gradient):
+The harness is this project's own: a ``SlotSchedule`` decides which slot
+each fill goes to, a ``WeightSource`` owns the slots (or hands every layer its
+own buffer), and a ``Block`` runs one layer from the weights the source
+materialises.  One training step multiplies every layer's input by a
+trainable gain vector, runs the blocks under non-reentrant checkpointing and
+back-propagates a fixed random projection of the output.  The gains'
+gradients are computed from the weights in the backward, so they expose
+which bytes the backward read.
 
-* ``fused``: ``nf4_linear`` (the fused kernels, every field saved through
-  ``save_for_backward``);
-* ``dense``: the same layers as dense bf16 ``W_hat`` through ``F.linear`` --
-  the control showing that the harness itself is sound;
+Arms, each run with reused slots and with a private buffer per layer:
+
+* ``fused``: ``nf4_linear`` (every field through ``save_for_backward``);
+* ``dense``: the same layers as dense bf16 ``W_hat`` through ``F.linear``
+  (the control that shows the harness is sound);
 * ``ctx_held``: the negative control, the same fused kernels behind a
-  Function that keeps the weight fields on ctx.  Under recycling only the
-  last ``slots`` layers may come out right.
+  Function that keeps the weight fields on ctx (the #2034 pattern).
 
-A layer is the seven projections of a Qwen-32B-shaped block in nested NF4
-(about 240 MiB of packed fields), above the ~165 MiB per layer at which
-Soup #842 ("The constraint: #331") saw the wrong gradients.  Each projection
-consumes either the layer input h or another projection's output, and the
-layer's output is a fixed linear combination of them, so nothing after the
-slot copy is saved by autograd except what the projection wrappers save --
-the non-reentrant recompute therefore replays the slot copy exactly when the
-wrapper saved its weight fields (Soup #842 and #1999 describe the recompute
-stopping early once the last saved tensor is rebuilt).
+A layer is a Qwen-32B-shaped block of seven projections in nested NF4 (about
+240 MiB of packed fields), above the ~165 MiB per layer at which Soup #842
+("The constraint: #331") saw wrong gradients.
 
-Run as a script on a GPU to print the per-layer table:
+Run as a script on a GPU for the per-layer summary:
     python tests/aliasing_harness.py
 """
 
@@ -39,7 +40,8 @@ from __future__ import annotations
 
 import os
 import sys
-from dataclasses import dataclass
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List, Optional
 
 if __name__ == "__main__":                       # run as a script: the repository root holds the packages
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
@@ -51,205 +53,238 @@ from torch.utils.checkpoint import checkpoint
 import workloads as WL
 from nf4_bit_weight_amd import api
 from nf4_bit_weight_amd.autograd import nf4_linear
-from nf4_bit_weight_amd.streaming import LayerBuffer
+from nf4_bit_weight_amd.streaming import ALIGN, LayerBuffer
 
-ALIGN = 256          # alignment of every dense block inside a layer buffer
-
-
-def _round_up(n: int) -> int:
-    return (n + ALIGN - 1) // ALIGN * ALIGN
+ARMS = ("fused", "dense", "ctx_held")
 
 
-# One layer's NF4 fields in a single byte buffer, so a slot copy moves the
-# whole layer with one copy_; views(buf) rebuilds the projections on a slot.
-PackedLayer = LayerBuffer
+class DenseBlockStore:
+    """A layer's dense bf16 W_hat blocks [N, K] in one flat buffer, each block
+    starting on an ALIGN-byte boundary (the dense twin of ``LayerBuffer``)."""
 
-
-class DenseLayer:
-    """The same layer as dense bf16 W_hat [N, K] blocks in one buffer."""
-
-    def __init__(self, names, dense):
+    def __init__(self, names, blocks: List[torch.Tensor]):
         self.names = list(names)
-        self.shapes = [tuple(d.shape) for d in dense]
-        self.offsets = []
-        off = 0
-        for d in dense:
-            self.offsets.append(off)
-            off += _round_up(d.numel())
-        self.store = torch.empty(off, dtype=torch.bfloat16, device=dense[0].device)
-        for d, o in zip(dense, self.offsets):
-            self.store[o:o + d.numel()].copy_(d.reshape(-1))
+        self.shapes = [tuple(b.shape) for b in blocks]
+        step = ALIGN // 2                               # bf16 elements per ALIGN bytes
+        starts, pos = [], 0
+        for b in blocks:
+            starts.append(pos)
+            pos += -(-b.numel() // step) * step
+        self.starts = starts
+        self.store = torch.zeros(pos, dtype=torch.bfloat16, device=blocks[0].device)
+        for b, s in zip(blocks, starts):
+            self.store.narrow(0, s, b.numel()).copy_(b.flatten())
 
-    def views(self, buf: torch.Tensor) -> dict:
-        return {n: buf[o:o + s[0] * s[1]].view(s) for n, o, s in zip(self.names, self.offsets, self.shapes)}
+    @property
+    def nbytes(self) -> int:
+        return self.store.numel() * 2
+
+    def views(self, buf: torch.Tensor) -> Dict[str, torch.Tensor]:
+        return {n: buf.narrow(0, s, r * c).view(r, c)
+                for n, s, (r, c) in zip(self.names, self.starts, self.shapes)}
 
 
-class SlotRing:
-    """Round-robin recycled device buffers: every ``acquire`` copies the
-    source into the next slot and hands that slot out, so a slot given out in
-    the original forward is overwritten later in the same step."""
+class SlotSchedule:
+    """Which of ``n`` slots the next fill goes to: fill number f uses slot
+    f mod n.  The count runs on across the forward and the recompute, as a
+    streaming caller's does, so the recompute of a layer generally lands in
+    a different slot than its forward did."""
 
-    def __init__(self, n_slots: int, like: torch.Tensor):
-        self.slots = [torch.empty_like(like) for _ in range(n_slots)]
-        self.cursor = 0
+    def __init__(self, n: int):
+        if n < 1:
+            raise ValueError("at least one slot")
+        self.n = n
+        self.fills = 0
 
-    def acquire(self, src: torch.Tensor) -> torch.Tensor:
-        slot = self.slots[self.cursor % len(self.slots)]
-        self.cursor += 1
-        slot.copy_(src)
-        return slot
+    def next_slot(self) -> int:
+        k = self.fills % self.n
+        self.fills += 1
+        return k
+
+
+class WeightSource:
+    """Materialises a layer's weights for one visit.  Reused mode: the layer's
+    bytes are copied into the slot the schedule names and views of that slot
+    are returned.  Private mode: views of the layer's own buffer, nothing is
+    ever overwritten."""
+
+    def __init__(self, stores, reuse: bool, n_slots: int):
+        self.stores = list(stores)
+        self.reuse = reuse
+        self.schedule = SlotSchedule(n_slots)
+        if reuse:
+            size = max(s.store.numel() for s in self.stores)
+            proto = self.stores[0].store
+            self.slots = [torch.empty(size, dtype=proto.dtype, device=proto.device)
+                          for _ in range(n_slots)]
+        else:
+            self.slots = []
+
+    def weights(self, layer: int) -> dict:
+        src = self.stores[layer]
+        if not self.reuse:
+            return src.views(src.store)
+        dst = self.slots[self.schedule.next_slot()].narrow(0, 0, src.store.numel())
+        dst.copy_(src.store)
+        return src.views(dst)
 
 
 class CtxHeldNF4MatMul(torch.autograd.Function):
-    """Negative control: the same fused kernels, with the weight fields kept
-    on ctx as plain attributes instead of ``save_for_backward`` (the pattern
-    bitsandbytes #2034 "Root cause" describes).  Checkpointing never sees
-    them, so a recycled slot is read back as whatever it holds at backward
-    time.  Never use this outside the harness."""
+    """Negative control: the fused kernels with the weight fields kept on ctx
+    as an attribute instead of through ``save_for_backward`` (the pattern of
+    bitsandbytes #2034 "Root cause").  Checkpointing never re-materialises
+    them, so a reused slot is read back with whatever it holds at backward
+    time.  Only for this harness."""
 
     @staticmethod
-    def forward(ctx, x, w_holder):
-        w = w_holder[0]
-        ctx.w = w
-        return api.nf4_matmul_fwd(x.contiguous(), w)
+    def forward(ctx, x, holder):
+        ctx.weight = holder[0]
+        return api.nf4_matmul_fwd(x.contiguous(), holder[0])
 
     @staticmethod
     def backward(ctx, grad_y):
-        return api.nf4_matmul_bwd_input(grad_y.contiguous(), ctx.w), None
+        return api.nf4_matmul_bwd_input(grad_y.contiguous(), ctx.weight), None
 
 
-def _linear(arm: str):
-    if arm == "fused":
-        return nf4_linear
-    if arm == "ctx_held":
-        return lambda x, w: CtxHeldNF4MatMul.apply(x, [w])
-    if arm == "dense":
-        return F.linear
-    raise ValueError(arm)
+def projection(arm: str) -> Callable:
+    return {
+        "fused": nf4_linear,
+        "dense": F.linear,
+        "ctx_held": lambda x, w: CtxHeldNF4MatMul.apply(x, [w]),
+    }[arm]
 
 
-def layer_forward(x, h, weights: dict, lin):
-    """One block after its trainable scale (h = x * scale, computed upstream
-    of the weight copy, so the scale's gradient is computed from W in the
-    backward): the seven projections combined linearly.  k and v (N = 1024)
-    are tiled back to the model width as grouped-query heads are."""
-    q = lin(h, weights["q"])
-    k = lin(h, weights["k"])
-    v = lin(h, weights["v"])
-    a = lin(q, weights["o"])
-    g = lin(h, weights["gate"]) + lin(h, weights["up"])
-    d = lin(g, weights["down"])
-    rep = q.shape[1] // k.shape[1]
-    return x + 0.05 * (a + d + (k + v).repeat(1, rep))
+def mix(x, u, w: dict, lin) -> torch.Tensor:
+    """One block on the gained input u: attention-like q -> o, grouped k/v
+    heads tiled to the width, a gate/up sum -> down, added to the residual x
+    with a small weight.  Every projection reads u or another projection's
+    output, so the block saves nothing weight-dependent outside the wrapper."""
+    q = lin(u, w["q"])
+    kv = lin(u, w["k"]) + lin(u, w["v"])
+    attn = lin(q, w["o"])
+    ffn = lin(lin(u, w["gate"]) + lin(u, w["up"]), w["down"])
+    heads = attn.shape[-1] // kv.shape[-1]
+    return x + 0.05 * (attn + ffn + kv.repeat(1, heads))
+
+
+class Block:
+    """Layer ``index`` as a function of (x, gain) for ``checkpoint``.  The
+    weights are materialised inside the call, i.e. inside the checkpointed
+    region: a recompute that runs this far materialises them again."""
+
+    def __init__(self, source: WeightSource, index: int, lin):
+        self.source, self.index, self.lin = source, index, lin
+
+    def __call__(self, x, gain):
+        u = torch.mul(x, gain)
+        return mix(x, u, self.source.weights(self.index), self.lin)
 
 
 @dataclass
-class HarnessModel:
-    nf4_layers: list
-    dense_layers: list
-    x: torch.Tensor
-    scales_init: list
+class Workload:
+    packed: list                     # LayerBuffer per layer
+    dense: list                      # DenseBlockStore per layer (may be empty)
+    x: torch.Tensor                  # [tokens, width] bf16 input
+    gains: list                      # initial gain vector per layer
+    probe: torch.Tensor              # [tokens, width] fp32 output projection
 
 
-def build(layers: int = 8, tokens: int = 256, projs=WL.QWEN_32B, seed: int = 0,
-          dense: bool = True, device="cuda") -> HarnessModel:
+@dataclass
+class StepResult:
+    loss: torch.Tensor
+    grads: List[torch.Tensor] = field(default_factory=list)   # one per gain, then the input's
+
+
+def make_workload(layers: int = 8, tokens: int = 256, projs=WL.QWEN_32B, seed: int = 0,
+                  dense: bool = True, device="cuda") -> Workload:
     """Seeded synthetic layers: weights 0.02 N(0,1) quantised to nested NF4
-    on the device; the dense control gets the dequantised W_hat of the same
+    on the device; the dense control holds the dequantised W_hat of the same
     weights, so both arms multiply by identical values."""
-    code = torch.from_numpy(WL.nf4_code_np()).to(device)
-    ncode = torch.from_numpy(WL.nested_code_np()).to(device)
+    dev = torch.device(device)
+    code = torch.from_numpy(WL.nf4_code_np()).to(dev)
+    ncode = torch.from_numpy(WL.nested_code_np()).to(dev)
     names = [p.name for p in projs]
-    nf4_layers, dense_layers = [], []
+    packed, dense_stores = [], []
     for l in range(layers):
-        ws, ds = [], []
+        qs = []
         for i, p in enumerate(projs):
-            w = WL.gpu_weight_f32(p.N, p.K, seed=80_000 + 100 * seed + 16 * l + i, device=device)
-            q = api.nf4_quantize(w, code, ncode)
+            w = WL.gpu_weight_f32(p.N, p.K, seed=80_000 + 100 * seed + 16 * l + i, device=dev)
+            qs.append(api.nf4_quantize(w, code, ncode))
             del w
-            ws.append(q)
-            if dense:
-                ds.append(api.nf4_dequantize(q))
-        nf4_layers.append(PackedLayer(names, ws))
-        del ws
+        packed.append(LayerBuffer(names, qs))
         if dense:
-            dense_layers.append(DenseLayer(names, ds))
-            del ds
+            dense_stores.append(DenseBlockStore(names, [api.nf4_dequantize(q) for q in qs]))
+        del qs
     width = projs[0].K
-    x = WL.gpu_normal_bf16(tokens, width, seed=81_000 + seed, device=device)
-    gen = torch.Generator(device=device)
+    x = WL.gpu_normal_bf16(tokens, width, seed=81_000 + seed, device=dev)
+    gen = torch.Generator(device=dev)
     gen.manual_seed(82_000 + seed)
-    scales = [(1.0 + 0.01 * torch.randn(width, generator=gen, device=device)).to(torch.bfloat16)
-              for _ in range(layers)]
+    gains = [(1.0 + 0.01 * torch.randn(width, generator=gen, device=dev)).to(torch.bfloat16)
+             for _ in range(layers)]
+    probe = torch.randn((tokens, width), generator=gen, device=dev) / tokens
     torch.cuda.synchronize()
-    return HarnessModel(nf4_layers, dense_layers, x, scales)
+    return Workload(packed, dense_stores, x, gains, probe)
 
 
-def run(model: HarnessModel, arm: str, recycle: bool, slots: int = 2, use_checkpoint: bool = True,
-        early_stop: bool = True):
-    """One forward + backward through every layer.  Returns (loss, grads)
-    with grads = [grad of each layer's scale] + [grad of the input].
+def train_step(work: Workload, arm: str, reuse: bool, slots: int = 2, checkpointed: bool = True,
+               early_stop: bool = True) -> StepResult:
+    """Forward through every block, then the backward of <probe, output>.
 
-    With early stop (torch's default), a layer's recompute ends once the
-    tensors its forward saved are rebuilt: for the negative control that is
-    before the slot copy, so the slots keep their last forward contents and
-    the last ``slots`` layers come out right.  Without it every recompute
-    replays the copy before the ctx-held backward reads the slot, and only
-    the last layer does."""
-    layers = model.dense_layers if arm == "dense" else model.nf4_layers
-    ring = SlotRing(slots, layers[0].store) if recycle else None
-    lin = _linear(arm)
-    params = [s.clone().requires_grad_(True) for s in model.scales_init]
-    x0 = model.x.clone().requires_grad_(True)
-
-    def body(idx):
-        def fn(x, scale):
-            h = x * scale                      # trainable, before the weight copy
-            # the copy sits inside the checkpointed region: a recompute that
-            # runs past this point copies the layer into the next slot again
-            buf = ring.acquire(layers[idx].store) if recycle else layers[idx].store
-            return layer_forward(x, h, layers[idx].views(buf), lin)
-        return fn
-
-    x = x0
-    for i in range(len(layers)):
-        if use_checkpoint:
-            x = checkpoint(body(i), x, params[i], use_reentrant=False, early_stop=early_stop)
+    With early stop (torch's default) a block's recompute ends once the
+    tensors its forward saved are rebuilt.  For the negative control that
+    happens before the weights are materialised again, so the slots keep
+    their forward contents and the last ``slots`` layers come out right.
+    Without early stop every recompute refills a slot before the ctx-held
+    backward reads it, and only the last layer is right."""
+    stores = work.dense if arm == "dense" else work.packed
+    source = WeightSource(stores, reuse, slots)
+    lin = projection(arm)
+    gains = [g.clone().requires_grad_(True) for g in work.gains]
+    x_in = work.x.clone().requires_grad_(True)
+    act = x_in
+    for index, gain in enumerate(gains):
+        block = Block(source, index, lin)
+        if checkpointed:
+            act = checkpoint(block, act, gain, use_reentrant=False, early_stop=early_stop)
         else:
-            x = body(i)(x, params[i])
-    loss = x.float().pow(2).mean()
-    loss.backward()
+            act = block(act, gain)
+    objective = torch.sum(act.float() * work.probe)
+    objective.backward()
     torch.cuda.synchronize()
-    return loss.detach().clone(), [p.grad.detach().clone() for p in params] + [x0.grad.detach().clone()]
+    grads = [g.grad.detach().clone() for g in gains] + [x_in.grad.detach().clone()]
+    return StepResult(objective.detach().clone(), grads)
 
 
-def max_abs_diffs(a, b):
-    return [float((u.float() - v.float()).abs().max().item()) for u, v in zip(a, b)]
+def grad_gaps(a: StepResult, b: StepResult) -> List[float]:
+    """max |a - b| per gradient (the gains in layer order, then the input)."""
+    return [float(torch.max(torch.abs(u.float() - v.float())).item()) for u, v in zip(a.grads, b.grads)]
 
 
-def table(model: HarnessModel, slots: int = 2):
-    """{arm: (loss recycled == loss private, per-layer max |grad diff|)}."""
+def compare_arms(work: Workload, slots: int = 2) -> Dict[str, dict]:
+    """Per arm: whether the loss is bit-equal between reused and private
+    buffers, and the per-gradient gaps between the two."""
     out = {}
-    for arm in ("fused", "dense", "ctx_held"):
-        if arm == "dense" and not model.dense_layers:
+    for arm in ARMS:
+        if arm == "dense" and not work.dense:
             continue
-        lp, gp = run(model, arm, recycle=False, slots=slots)
-        lr, gr = run(model, arm, recycle=True, slots=slots)
-        out[arm] = (bool(torch.equal(lp, lr)), max_abs_diffs(gr, gp))
+        private = train_step(work, arm, reuse=False, slots=slots)
+        reused = train_step(work, arm, reuse=True, slots=slots)
+        out[arm] = {"loss_equal": bool(torch.equal(private.loss, reused.loss)),
+                    "gaps": grad_gaps(reused, private)}
     return out
 
 
-def main(argv):
-    model = build()
-    mib = model.nf4_layers[0].nbytes / 2 ** 20
-    res = table(model)
-    print(f"layer buffer: {mib:.1f} MiB nested NF4, 2 slots for {len(model.nf4_layers)} layers")
-    print(f"{'layer':>5}  " + "  ".join(f"{a + ' recycled vs private':>28}" for a in res))
-    n = len(model.nf4_layers)
-    for i in range(n + 1):
-        name = str(i) if i < n else "x"
-        print(f"{name:>5}  " + "  ".join(f"{d[i]:>22.6e} {'MISMATCH' if d[i] else '  ok    '}"
-                                         for (_, d) in res.values()))
-    print("forward loss bit-equal: " + ", ".join(f"{a}={e}" for a, (e, _) in res.items()))
+def main(argv) -> int:
+    slots = int(argv[0]) if argv else 2
+    work = make_workload()
+    res = compare_arms(work, slots)
+    n = len(work.packed)
+    print(f"{n} layers of {work.packed[0].nbytes / 2 ** 20:.1f} MiB nested NF4 through {slots} reused slots")
+    for arm, r in res.items():
+        exact = [i for i, g in enumerate(r["gaps"][:n]) if g == 0.0]
+        worst = max(r["gaps"])
+        print(f"  {arm:>9}: loss bit-equal {r['loss_equal']}; layers with exact gain gradients "
+              f"{exact or 'none'}; input gradient gap {r['gaps'][n]:.3e}; largest gap {worst:.3e}")
     return 0
 
 

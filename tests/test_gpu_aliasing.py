@@ -3,7 +3,7 @@
 bitsandbytes issue #2034 ("Minimal reproducer", "What it prints", "Why
 save_for_backward fixes it") and Soup issue #842 ("Acceptance criteria"):
 
-* with 2 recycled slots for 8 Qwen-32B-shaped layers (~240 MiB of nested NF4
+* with 2 reused slots for 8 Qwen-32B-shaped layers (~240 MiB of nested NF4
   each, above the ~165 MiB of Soup #842 "The constraint: #331"), the fused
   wrapper's gradients are bit-identical to those with a private buffer per
   layer, and so are the dense bf16 control's;
@@ -34,31 +34,32 @@ LAYERS = 8
 
 @pytest.fixture(scope="module")
 def model():
-    m = AH.build(layers=LAYERS, tokens=256)
+    m = AH.make_workload(layers=LAYERS, tokens=256)
     yield m
     del m
     torch.cuda.empty_cache()
 
 
 def test_layer_size_above_threshold(model):
-    assert model.nf4_layers[0].nbytes > 165 * 2 ** 20
+    assert model.packed[0].nbytes > 165 * 2 ** 20
 
 
 @pytest.mark.parametrize("arm", ["fused", "dense"])
-def test_recycled_equals_private(model, arm):
-    lp, gp = AH.run(model, arm, recycle=False)
-    lr, gr = AH.run(model, arm, recycle=True)
-    assert torch.equal(lp, lr), f"{arm}: forward loss differs"
-    for i, (a, b) in enumerate(zip(gr, gp)):
-        assert torch.equal(a, b), f"{arm}: gradient {i} differs under recycling"
+def test_reused_equals_private(model, arm):
+    p = AH.train_step(model, arm, reuse=False)
+    r = AH.train_step(model, arm, reuse=True)
+    assert torch.equal(p.loss, r.loss), f"{arm}: forward loss differs"
+    for i, (a, b) in enumerate(zip(r.grads, p.grads)):
+        assert torch.equal(a, b), f"{arm}: gradient {i} differs with reused slots"
 
 
 @pytest.mark.parametrize("slots", [2, 3])
 def test_negative_control_pattern(model, slots):
-    lp, gp = AH.run(model, "ctx_held", recycle=False, slots=slots)
-    lr, gr = AH.run(model, "ctx_held", recycle=True, slots=slots)
-    assert torch.equal(lp, lr), "forward must stay bit-exact"
-    d = AH.max_abs_diffs(gr, gp)
+    p = AH.train_step(model, "ctx_held", reuse=False, slots=slots)
+    r = AH.train_step(model, "ctx_held", reuse=True, slots=slots)
+    assert torch.equal(p.loss, r.loss), "forward must stay bit-exact"
+    gp = p.grads
+    d = AH.grad_gaps(r, p)
     for i in range(LAYERS - slots):
         # wrong by far more than rounding: another layer's weights were used
         rel = d[i] / float(gp[i].float().abs().max().item())
@@ -67,7 +68,7 @@ def test_negative_control_pattern(model, slots):
         assert d[i] == 0.0, f"layer {i}: slot not yet recycled, must be exact"
     assert d[LAYERS] > 0.0, "input gradient passes through recycled layers"
     # with private buffers the two wrappers run the same kernels on the same bytes
-    _, gf = AH.run(model, "fused", recycle=False, slots=slots)
+    gf = AH.train_step(model, "fused", reuse=False, slots=slots).grads
     for i, (a, b) in enumerate(zip(gf, gp)):
         assert torch.equal(a, b), f"private arms differ at {i}"
 
@@ -75,34 +76,34 @@ def test_negative_control_pattern(model, slots):
 def test_without_early_stop(model):
     # every recompute replays the slot copy: the wrapper stays exact, the
     # negative control now reads the next layer's bytes everywhere but last
-    lp, gp = AH.run(model, "fused", recycle=False, early_stop=False)
-    lr, gr = AH.run(model, "fused", recycle=True, early_stop=False)
-    assert torch.equal(lp, lr)
-    assert all(torch.equal(a, b) for a, b in zip(gr, gp))
-    _, cp = AH.run(model, "ctx_held", recycle=False, early_stop=False)
-    _, cr = AH.run(model, "ctx_held", recycle=True, early_stop=False)
-    d = AH.max_abs_diffs(cr, cp)
+    p = AH.train_step(model, "fused", reuse=False, early_stop=False)
+    r = AH.train_step(model, "fused", reuse=True, early_stop=False)
+    assert torch.equal(p.loss, r.loss)
+    assert all(torch.equal(a, b) for a, b in zip(r.grads, p.grads))
+    cp = AH.train_step(model, "ctx_held", reuse=False, early_stop=False)
+    cr = AH.train_step(model, "ctx_held", reuse=True, early_stop=False)
+    d = AH.grad_gaps(cr, cp)
     assert all(v > 0 for v in d[:LAYERS - 1]) and d[LAYERS - 1] == 0.0, d
 
 
 def test_version_counter_catches_overwrite(model):
-    l0, l1 = model.nf4_layers[0], model.nf4_layers[1]
+    l0, l1 = model.packed[0], model.packed[1]
     slot = l0.store.clone()
     x = model.x.clone().requires_grad_(True)
     y = nf4_linear(x, l0.views(slot)["q"])
     slot.copy_(l1.store)                                 # in-place overwrite of the saved bytes
     with pytest.raises(RuntimeError, match="modified by an inplace operation"):
-        y.float().pow(2).sum().backward()
+        torch.sum(y.float() ** 2).backward()
 
     # the negative control computes with whatever the slot now holds
     slot.copy_(l0.store)
     xr = model.x.clone().requires_grad_(True)
     yr = nf4_linear(xr, l0.views(l0.store)["q"])
-    yr.float().pow(2).sum().backward()
+    torch.sum(yr.float() ** 2).backward()
     xc = model.x.clone().requires_grad_(True)
     yc = AH.CtxHeldNF4MatMul.apply(xc, [l0.views(slot)["q"]])
     slot.copy_(l1.store)
-    yc.float().pow(2).sum().backward()
+    torch.sum(yc.float() ** 2).backward()
     torch.cuda.synchronize()
     assert torch.equal(yc, yr), "forward identical"
     assert not torch.equal(xc.grad, xr.grad), "negative control must be silently wrong"
@@ -121,7 +122,7 @@ def _audit(fn):
 
 
 def test_saved_tensors_audit_linear(model):
-    lay = model.nf4_layers[0]
+    lay = model.packed[0]
     w = lay.views(lay.store)["gate"]
     N, K = w.N, w.K
     x = model.x.clone().requires_grad_(True)

@@ -2,8 +2,8 @@
 
 The layer buffer (used by the aliasing harness and the layer streamer) must
 reproduce every field bit for bit through its views and keep every field
-aligned; the harness's slot ring must hand out slots round-robin,
-overwriting the one handed out ``n_slots`` acquires earlier.
+aligned; the harness's slot schedule must send fill f to slot f mod n, so a
+reused slot holds the bytes of the latest fill that landed in it.
 """
 
 import numpy as np
@@ -30,7 +30,7 @@ def _fake_weight(N, K, seed, nested=True):
 def test_packed_layer_roundtrip_and_alignment():
     for nested in (True, False):
         ws = [_fake_weight(N, K, i, nested) for i, (N, K) in enumerate([(128, 192), (64, 4160), (200, 64)])]
-        lay = AH.PackedLayer(["a", "b", "c"], ws)
+        lay = streaming.LayerBuffer(["a", "b", "c"], ws)
         for buf in (lay.store, lay.store.clone()):
             views = lay.views(buf)
             for name, w in zip("abc", ws):
@@ -48,27 +48,35 @@ def test_packed_layer_roundtrip_and_alignment():
 
 def test_views_alias_the_buffer():
     ws = [_fake_weight(64, 128, 7)]
-    lay = AH.PackedLayer(["a"], ws)
+    lay = streaming.LayerBuffer(["a"], ws)
     buf = lay.store.clone()
     v = lay.views(buf)["a"]
     buf.zero_()
     assert int(v.packed.sum()) == 0 and int(v.absmax.sum()) == 0
 
 
-def test_dense_layer_views():
+def test_dense_block_store_views():
     d = [torch.randn(8, 16).to(torch.bfloat16), torch.randn(3, 5).to(torch.bfloat16)]
-    lay = AH.DenseLayer(["x", "y"], d)
+    lay = AH.DenseBlockStore(["x", "y"], d)
     v = lay.views(lay.store)
     assert torch.equal(v["x"], d[0]) and torch.equal(v["y"], d[1])
+    assert all((s * 2) % streaming.ALIGN == 0 for s in lay.starts)
 
 
-def test_slot_ring_round_robin():
-    src = [torch.full((4,), float(i)) for i in range(5)]
-    ring = AH.SlotRing(2, src[0])
-    got = [ring.acquire(s) for s in src]
-    assert got[0] is got[2] is got[4] and got[1] is got[3]
-    # what a holder of the first slot sees after the later acquires
-    assert torch.equal(got[0], src[4]) and torch.equal(got[1], src[3])
+def test_slot_schedule_and_weight_source():
+    sched = AH.SlotSchedule(3)
+    assert [sched.next_slot() for _ in range(7)] == [0, 1, 2, 0, 1, 2, 0]
+    d = [[torch.full((4, 4), float(i)).to(torch.bfloat16)] for i in range(5)]
+    stores = [AH.DenseBlockStore(["w"], b) for b in d]
+    src = AH.WeightSource(stores, reuse=True, n_slots=2)
+    got = [src.weights(i)["w"] for i in range(5)]
+    # fills 0, 2, 4 share slot 0 and fills 1, 3 slot 1: an early holder sees the latest fill
+    assert got[0].data_ptr() == got[2].data_ptr() == got[4].data_ptr()
+    assert got[1].data_ptr() == got[3].data_ptr() != got[0].data_ptr()
+    assert torch.equal(got[0], d[4][0]) and torch.equal(got[1], d[3][0])
+    own = AH.WeightSource(stores, reuse=False, n_slots=2)
+    assert [float(own.weights(i)["w"][0, 0]) for i in range(5)] == [0.0, 1.0, 2.0, 3.0, 4.0]
+    assert own.weights(2)["w"].data_ptr() == stores[2].store.data_ptr()
 
 
 def test_layer_buffer_rejects_small_or_wrong_buffers():
