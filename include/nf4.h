@@ -92,6 +92,7 @@ extern "C" {
 #define NF4_ERR_WORKSPACE    -5  /* workspace missing or smaller than required     */
 #define NF4_ERR_HIP          -6  /* the HIP runtime reported an error on launch    */
 #define NF4_ERR_DTYPE        -7  /* unknown dtype selector                          */
+#define NF4_ERR_SCRATCH      -8  /* needs more scratch than the fixed buffer holds  */
 
 /* ---- dtype selectors ---------------------------------------------------- */
 #define NF4_DTYPE_F32  0
@@ -212,6 +213,33 @@ int nf4_grouped_matmul_bwd_input(const void* grad_y, const int32_t* offsets,
                                  const float* code16, const float* nested_code256,
                                  int64_t N, int64_t K, void* grad_x, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/*
+ * nf4_matmul_fwd_noalloc -- nf4_matmul_fwd without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *   Same arguments, result and kernels as nf4_matmul_fwd (bitwise identical
+ *   output), minus ws / ws_bytes.  The split-contraction partials go to a
+ *   fixed device array of NF4_NOALLOC_SCRATCH_BYTES inside the library; each
+ *   GPU the library runs on holds its own copy until the process ends.  Its
+ *   address is looked up once per device (with hipGetSymbolAddress) on the
+ *   first call made while that device is current; the call runs on the
+ *   current device, and `stream` must belong to it.
+ *   Allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ *   A product whose plan needs more than NF4_NOALLOC_SCRATCH_BYTES of
+ *   partials (nf4_workspace_bytes(NF4_OP_MATMUL_FWD, ...) larger than it)
+ *   returns NF4_ERR_SCRATCH and enqueues nothing.
+ *   All calls on one GPU share its array, and every partial is written
+ *   before it is read, so nothing needs clearing between calls; two calls
+ *   that overlap on one GPU (different streams, no ordering) race on it.
+ */
+#define NF4_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int nf4_matmul_fwd_noalloc(const void* x, int64_t M,
+                           const uint8_t* packed, const void* absmax,
+                           const float* nested_absmax, const float* nested_offset,
+                           const float* code16, const float* nested_code256,
+                           int64_t N, int64_t K, void* y, void* stream);
 
 /* ---- host-only helpers (no device work) --------------------------------- */
 

@@ -22,6 +22,9 @@ NF4_ERR_ALIGN = -4
 NF4_ERR_WORKSPACE = -5
 NF4_ERR_HIP = -6
 NF4_ERR_DTYPE = -7
+NF4_ERR_SCRATCH = -8
+
+NF4_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 NF4_DTYPE_F32 = 0
 NF4_DTYPE_BF16 = 1
@@ -49,6 +52,7 @@ SIGNATURES = {
     "nf4_dequantize": (_int, [*_W, _int, _vp, _vp]),
     "nf4_matmul_fwd": (_int, [_vp, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_matmul_bwd_input": (_int, [_vp, _i64, *_W, _vp, _vp, _size, _vp]),
+    "nf4_matmul_fwd_noalloc": (_int, [_vp, _i64, *_W, _vp, _vp]),
     "nf4_grouped_matmul_fwd": (_int, [_vp, _vp, _i32, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_grouped_matmul_bwd_input": (_int, [_vp, _vp, _i32, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_workspace_bytes": (_size, [_int, _i64, _i64, _i64, _i32]),

@@ -3,6 +3,7 @@
 // allocates, frees or synchronises.
 #include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "../../include/nf4.h"
 #include "nf4_internal.hpp"
@@ -10,6 +11,12 @@
 namespace nf4 {
 
 static std::atomic<int64_t> g_path_counts[NF4_PATH_COUNT];
+
+// The fixed device buffer of nf4_matmul_fwd_noalloc (split-contraction
+// partials).  In host code its name is only a stand-in for registration: the
+// device address is obtained per device with hipGetSymbolAddress and only
+// that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[NF4_NOALLOC_SCRATCH_BYTES];
 
 void count_path(int path) {
   if (path >= 0 && path < NF4_PATH_COUNT) g_path_counts[path].fetch_add(1, std::memory_order_relaxed);
@@ -63,10 +70,38 @@ hipError_t zero_bf16(void* out, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per
+// device while it is current.  hipGetSymbolAddress allocates nothing.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return NF4_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return NF4_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return NF4_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NF4_OK;
+}
+
+// fixed_scratch: ws is the library's own fixed buffer of ws_bytes; a plan
+// that needs more is NF4_ERR_SCRATCH rather than a caller workspace error.
 int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed,
                   const void* absmax, const float* nested_absmax, const float* nested_offset,
                   const float* code16, const float* ncode, int64_t N, int64_t K, void* C,
-                  void* ws, size_t ws_bytes, void* stream) {
+                  void* ws, size_t ws_bytes, void* stream, bool fixed_scratch = false) {
   const bool bwd = kind == GemmKind::kBwdInput;
   int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K);
   if (st) return st;
@@ -86,6 +121,12 @@ int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed
     return NF4_OK;
   }
   const GemmPlan plan = plan_gemm(kind, M, N, K, device_cu_count());
+  if (fixed_scratch) {
+    if (plan.ws_bytes > ws_bytes) return NF4_ERR_SCRATCH;
+    // set-up on the first call that reaches a launch on this device
+    const int sst = scratch_for_current_device(&ws);
+    if (sst) return sst;
+  }
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return NF4_ERR_WORKSPACE;
   if (plan.ws_bytes > 0 && !aligned16(ws)) return NF4_ERR_ALIGN;
   const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
@@ -178,6 +219,15 @@ int nf4_matmul_fwd(const void* x, int64_t M, const uint8_t* packed, const void* 
                        code16, nested_code256, N, K, y, ws, ws_bytes, stream);
 }
 
+int nf4_matmul_fwd_noalloc(const void* x, int64_t M, const uint8_t* packed, const void* absmax,
+                           const float* nested_absmax, const float* nested_offset,
+                           const float* code16, const float* nested_code256, int64_t N, int64_t K,
+                           void* y, void* stream) {
+  return matmul_common(GemmKind::kFwd, x, M, packed, absmax, nested_absmax, nested_offset, code16,
+                       nested_code256, N, K, y, nullptr, NF4_NOALLOC_SCRATCH_BYTES, stream,
+                       /*fixed_scratch=*/true);
+}
+
 int nf4_matmul_bwd_input(const void* grad_y, int64_t M, const uint8_t* packed,
                          const void* absmax, const float* nested_absmax,
                          const float* nested_offset, const float* code16,
@@ -263,6 +313,9 @@ const char* nf4_status_str(int status) {
     case NF4_ERR_WORKSPACE: return "NF4_ERR_WORKSPACE: workspace missing or too small";
     case NF4_ERR_HIP: return "NF4_ERR_HIP: the HIP runtime reported an error";
     case NF4_ERR_DTYPE: return "NF4_ERR_DTYPE: unknown dtype selector";
+    case NF4_ERR_SCRATCH:
+      return "NF4_ERR_SCRATCH: the product needs more split partials than the fixed scratch buffer "
+             "of nf4_matmul_fwd_noalloc holds (NF4_NOALLOC_SCRATCH_BYTES); use nf4_matmul_fwd with a workspace";
     default: return "unknown NF4 status";
   }
 }

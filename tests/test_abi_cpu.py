@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, f"binding lacks {n}"
@@ -44,7 +44,7 @@ def test_header_macros_match_binding():
     text = open(HEADER).read()
     vals = dict(re.findall(r"#define\s+(NF4_[A-Z0-9_]+)\s+(-?\d+)", text))
     for name in ("NF4_OK", "NF4_ERR_NULL", "NF4_ERR_SHAPE", "NF4_ERR_UNSUPPORTED",
-                 "NF4_ERR_ALIGN", "NF4_ERR_WORKSPACE", "NF4_ERR_HIP", "NF4_ERR_DTYPE",
+                 "NF4_ERR_ALIGN", "NF4_ERR_WORKSPACE", "NF4_ERR_HIP", "NF4_ERR_DTYPE", "NF4_ERR_SCRATCH",
                  "NF4_DTYPE_F32", "NF4_DTYPE_BF16", "NF4_OP_QUANTIZE", "NF4_OP_MATMUL_FWD",
                  "NF4_OP_MATMUL_BWD_INPUT", "NF4_OP_GROUPED_FWD", "NF4_OP_GROUPED_BWD_INPUT"):
         assert int(vals[name]) == getattr(L, name), name
@@ -61,7 +61,7 @@ def test_storage_helpers_match_oracle(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = L.status_str(code)
         assert s.startswith("NF4_"), s
     assert L.status_str(-99) == "unknown NF4 status"
@@ -163,3 +163,19 @@ def test_no_memset_in_library_sources():
         text = open(os.path.join(csrc, name)).read()
         code = re.sub(r"//[^\n]*", "", re.sub(r"/\*.*?\*/", "", text, flags=re.S))
         assert not re.search(r"\bhipMemset\w*\s*\(", code), f"{name} calls hipMemset"
+
+
+def test_noalloc_validation(lib):
+    """The no-allocation forward validates like nf4_matmul_fwd and refuses a
+    plan whose partials exceed its fixed buffer before touching the device."""
+    def f(x=FAKE, M=4, packed=FAKE, N=8, K=64, y=FAKE):
+        return lib.nf4_matmul_fwd_noalloc(x, M, packed, FAKE, None, None, FAKE, None, N, K, y, None)
+    assert f(x=None) == L.NF4_ERR_NULL
+    assert f(K=96) == L.NF4_ERR_UNSUPPORTED
+    assert f(M=0) == L.NF4_OK
+    M, N, K = 2048, 5120, 27648
+    assert lib.nf4_workspace_bytes(L.NF4_OP_MATMUL_FWD, M, N, K, 1) > L.NF4_NOALLOC_SCRATCH_BYTES
+    assert f(M=M, N=N, K=K) == L.NF4_ERR_SCRATCH
+    text = open(HEADER).read()
+    assert f"#define NF4_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert L.NF4_NOALLOC_SCRATCH_BYTES == 64 << 20
