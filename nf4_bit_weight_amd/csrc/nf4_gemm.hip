@@ -1491,8 +1491,10 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t nc = (kind == GemmKind::kFwd) ? N : K;
   const int64_t kc = (kind == GemmKind::kFwd) ? K : N;
   // Forward at M <= 32 streams the weights (nf4_gemv.hip) unless NF4_SMALL_M=0.
+  // The streaming kernel addresses a 16-row group of W with 32-bit offsets:
+  // rows of up to 2^26 elements.
   const char* sm = getenv("NF4_SMALL_M");
-  if (kind == GemmKind::kFwd && M <= 32 && !(sm && sm[0] == '0')) {
+  if (kind == GemmKind::kFwd && M <= 32 && K <= (int64_t{1} << 26) && !(sm && sm[0] == '0')) {
     plan_small_m(pl, M, N, K, cus);
     return pl;
   }

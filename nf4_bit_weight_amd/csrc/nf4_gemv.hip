@@ -76,6 +76,10 @@ struct Gv {
 template <int MP>
 using acc_t = typename std::conditional<MP == 16, f32x4_t, f32x16_t>::type;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <int N>
+using ic = std::integral_constant<int, N>;
+
 // Expand 8 nibbles in the order (0, 2, 4, 6, 1, 3, 5, 7): out[0] = (w0, w2),
 // out[1] = (w4, w6), out[2] = (w1, w3), out[3] = (w5, w7).
 __device__ __forceinline__ void expand8_eo(uint32_t p, const Lut& t, uint32_t (&out)[4]) {
@@ -406,6 +410,324 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   }
 }
 
+// ===========================================================================
+// Line-staged streaming kernel: 16-row W groups, x as one (M <= 16) or two
+// (M <= 32) 16-row halves.
+//
+// A wave owns one 16-row group of W and a contiguous run of 256-column steps
+// of the contraction chunk; lane (r = l % 16, g = l / 16) expands block g of
+// W row r in every step (one byte table, eight 8-nibble expansions) into the
+// B operand of eight v_mfma_f32_16x16x32_bf16 whose A operand is x.
+//
+// The packed bytes of a step (16 rows x 128 B) are copied global -> LDS by
+// two buffer_load_dwordx4 ... lds instructions, each covering 8 whole 128-byte
+// lines, into one of kSD private staging slots of the wave.  The 16-byte
+// pieces of row rr are stored at piece ^ ((rr >> 1) & 7), so the two 16-byte
+// reads of a lane's block hit distinct banks across each 16-lane group.  The
+// step's block scales (one per lane) arrive the same way, a byte or a dword
+// per lane.  Every load of the loop is such a copy, issued kSD steps ahead;
+// one explicit vmcnt per step is the only wait on memory, and a slot is only
+// refilled by the wave that reads it, so the loop has no barrier.  Two slots
+// per wave keep a workgroup's LDS small enough that the launches of the
+// decode shapes are resident in one round (measured: four slots halved the
+// resident workgroups and made the forward of gate at M = 1 18 us instead of
+// 15).  The buffer
+// resources carry the tensor bounds (reads past the end return zero) and move
+// with the step in scalar registers: the loop computes no vector addresses
+// except the nested-scale index.
+constexpr int kSD = 2;                          // staging slots per wave = copy distance (steps)
+constexpr int kSlotBytes = 2048 + 256 + 256;    // packed lines, block scales, nested scales
+constexpr int kLnMaxWaves = 8;
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
+
+// `bytes` > 0 (every copy starts inside its tensor); sizes from 2 GiB up are
+// clamped (the offsets a wave uses stay far below).  The test is on the high
+// bits so that it stays a scalar instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = static_cast<uint64_t>(bytes);
+  const uint32_t hi = static_cast<uint32_t>(b >> 32), lo = static_cast<uint32_t>(b);
+  const int32_t n = (hi | (lo >> 31)) != 0 ? 0x7FFFFFFF : static_cast<int32_t>(lo);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
+                                           kRsrcWord3);
+}
+
+template <int RW, int KW, bool NESTED, int MH>
+__global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
+  constexpr int kThr = 64 * RW * KW;
+  constexpr int C = NESTED ? 4 : 3;             // copy instructions per step
+  // [M + 1][kc + 8] bf16 (row M is zero), reused for the cross-wave sums;
+  // the waves' staging slots follow at byte p.tb_off
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ float sncode[256];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int rw = wave % RW, kw = wave / RW;
+  const int64_t N = p.w.N, K = p.w.K;
+  const int M = p.M;
+  const int z = blockIdx.y;
+  const int64_t k0 = static_cast<int64_t>(z) * p.kc;
+  const int64_t k1 = (k0 + p.kc < K) ? k0 + p.kc : K;
+  const int kc = p.kc;
+  const int pitch = kc + 8;
+
+  // this wave's steps of the chunk: a contiguous run
+  const int nsteps = static_cast<int>((k1 - k0 + 255) / 256);
+  const int per = (nsteps + KW - 1) / KW;
+  const int s_begin = kw * per < nsteps ? kw * per : nsteps;
+  const int s_end = s_begin + per < nsteps ? s_begin + per : nsteps;
+  const int nw = s_end - s_begin;
+
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t rg0 = (static_cast<int64_t>(blockIdx.x) * RW + rw) * 16;   // first W row of the group
+  const int64_t kb = K >> 6;                       // blocks per W row
+  const int64_t nb = N * kb;
+  const int64_t ng = (nb + kNestedBlock - 1) / kNestedBlock;
+
+  // ---- copy addressing (fixed per lane) --------------------------------------
+  const int lr = lane >> 3;                        // row within the 8 rows of one copy
+  auto piece = [](int row, int phys) { return phys ^ ((row >> 1) & 7); };
+  const uint32_t voff_w0 = static_cast<uint32_t>(lr * (K >> 1)) + 16u * piece(lr, lane & 7);
+  const uint32_t voff_w1 = static_cast<uint32_t>((8 + lr) * (K >> 1)) + 16u * piece(8 + lr, lane & 7);
+  const uint32_t lane_b = static_cast<uint32_t>(r * kb + g);      // block of the lane within the step
+  uint8_t* const slots = reinterpret_cast<uint8_t*>(xs) + p.tb_off + wave * (kSD * kSlotBytes);
+
+  auto issue = [&](int ls, int slot) {
+    const int st = s_begin + ls;                             // 0 <= st < nsteps
+    const int64_t kstep = k0 + 256 * static_cast<int64_t>(st);
+    uint8_t* const sl = slots + slot * kSlotBytes;
+    const int64_t wb = (rg0 * K + kstep) >> 1;               // first byte of the step's lines
+    const auto rw_ = rsrc(p.w.packed + wb, ((N * K) >> 1) - wb);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)sl, 16, voff_w0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)(sl + 1024), 16, voff_w1, 0, 0, 0);
+    const int64_t bb = rg0 * kb + (kstep >> 6);              // block of lane 0
+    if constexpr (NESTED) {
+      const auto ra = rsrc(static_cast<const uint8_t*>(p.w.absmax) + bb, nb - bb);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 1, lane_b, 0, 0, 0);
+      const int64_t bh = bb >> 8;
+      const uint32_t vn = ((static_cast<uint32_t>(bb & 255) + lane_b) >> 8) << 2;
+      const auto rn = rsrc(p.w.nested_absmax + bh, 4 * (ng - bh));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (lds_void_t*)(sl + 2304), 4, vn, 0, 0, 0);
+    } else {
+      const auto ra = rsrc(static_cast<const float*>(p.w.absmax) + bb, 4 * (nb - bb));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, 4u * lane_b, 0, 0, 0);
+    }
+  };
+  // Before step ls: the copies of step ls have landed once at most those of
+  // the later step already issued (ls + 1; none before the last step) are in
+  // flight.  vmcnt(c) with lgkmcnt and expcnt left open.
+  static_assert(kSD == 2, "wait counts below");
+  auto wait_copies = [&](int ls) {
+    if (ls + 1 < nw) __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | (15 << 8) | (7 << 4));
+    else __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));
+  };
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue ---------------------------------------------------------------
+  float code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
+  const float off = NESTED ? p.w.nested_offset[0] : 0.f;
+  // x[:, k0 : k0 + kc) in batches of kXB 16-byte chunks per thread, each
+  // 8-group stored as (0,2,4,6,1,3,5,7); row M and columns >= K are zero.
+  // Chunk c -> (row c / c8n, group c % c8n) by a float reciprocal with one
+  // correction each way (c < 2^24).  The first batch of x is loaded, then the
+  // copies of the first two steps are issued, then that batch is stored: the
+  // latencies of x and of the first weights overlap, and the wait for x
+  // (the older loads) leaves the copies in flight.
+  constexpr int kXB = 4;
+  const int c8n = kc / 8;
+  const int nchunks = (M + 1) * c8n;
+  const float inv_c8n = 1.0f / static_cast<float>(c8n);
+  u32x4_t xd[kXB];
+  int xoff[kXB];
+  auto x_load = [&](int base) {
+#pragma unroll
+    for (int j = 0; j < kXB; ++j) {
+      const int c = base + tid + j * kThr;
+      int m = static_cast<int>(static_cast<float>(c) * inv_c8n);
+      m -= (m * c8n > c) ? 1 : 0;
+      m += ((m + 1) * c8n <= c) ? 1 : 0;
+      const int c8 = c - m * c8n;
+      xoff[j] = c < nchunks ? m * pitch + 8 * c8 : -1;
+      xd[j] = u32x4_t{0u, 0u, 0u, 0u};
+      const int64_t k = k0 + 8 * c8;
+      if (c < nchunks && m < M && k < K)
+        xd[j] = *reinterpret_cast<const u32x4_t*>(p.x + static_cast<int64_t>(m) * K + k);
+    }
+  };
+  auto x_store = [&] {
+#pragma unroll
+    for (int j = 0; j < kXB; ++j) {
+      if (xoff[j] >= 0) {
+        const u32x4_t d = xd[j];
+        const u32x4_t o = {perm(d[1], d[0], 0x05040100u), perm(d[3], d[2], 0x05040100u),
+                           perm(d[1], d[0], 0x07060302u), perm(d[3], d[2], 0x07060302u)};
+        *reinterpret_cast<u32x4_t*>(xs + xoff[j]) = o;
+      }
+    }
+  };
+  // the nested table (256 entries over the workgroup's threads)
+  constexpr int kNC = (256 + kThr - 1) / kThr;
+  float nc_reg[kNC];
+  x_load(0);
+  if constexpr (NESTED) {
+#pragma unroll
+    for (int j = 0; j < kNC; ++j) nc_reg[j] = tid + j * kThr < 256 ? p.w.ncode[tid + j * kThr] : 0.f;
+  }
+  fence();
+  // Only copies that will be read are issued.  (Measured: a wave of one step
+  // that also issued a repeat copy of the same lines into its spare slot, to
+  // keep the count behind every step uniform, read stale data in 2-22% of
+  // runs after its counted wait; with exact counts and no repeated copy in
+  // flight, 0 of 200.)
+  if (nw > 0) issue(0, 0);
+  if (nw > 1) issue(1, 1);
+  fence();
+  // the x and table loads have returned once at most this wave's copies are in flight
+  if (nw > 1) __builtin_amdgcn_s_waitcnt(((2 * C) & 15) | (((2 * C) >> 4) << 14) | (15 << 8) | (7 << 4));
+  else if (nw == 1) __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | (15 << 8) | (7 << 4));
+  else __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));
+  if constexpr (NESTED) {
+#pragma unroll
+    for (int j = 0; j < kNC; ++j)
+      if (tid + j * kThr < 256) sncode[tid + j * kThr] = nc_reg[j];
+  }
+  x_store();
+  for (int base = kXB * kThr; base < nchunks; base += kXB * kThr) {
+    x_load(base);
+    x_store();
+  }
+  fence();
+  // x and the table are visible to every wave once their LDS writes are done;
+  // the weight copies go to each wave's own slots and are waited for per step
+  __builtin_amdgcn_s_waitcnt((7 << 4) | 0xC00F);           // lgkmcnt(0), vmcnt and expcnt open
+  __builtin_amdgcn_s_barrier();
+  fence();
+
+  acc_t<16> acc[MH];
+#pragma unroll
+  for (int h = 0; h < MH; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[h][i] = 0.f;
+
+  // A fragments: x row r (and r + 16), columns 64 g + 8 t of the step (rows >= M read the zero row)
+  const uint16_t* xrow[MH];
+#pragma unroll
+  for (int h = 0; h < MH; ++h) xrow[h] = xs + (r + 16 * h < M ? r + 16 * h : M) * pitch + 64 * g;
+  // LDS byte addresses of this lane's block pieces and scales in slot 0
+  const uint32_t sl0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)slots));
+  const uint32_t a_lo = sl0 + 16u * (8 * r + piece(r, 2 * g));
+  const uint32_t a_hi = sl0 + 16u * (8 * r + piece(r, 2 * g + 1));
+  const uint32_t a_sc = sl0 + 2048u + 4u * lane;
+
+  struct Staged {
+    u32x4_t lo, hi;
+    uint32_t sc, s2;
+  };
+#define NF4_LN_READ(OFF)                                                                   \
+  asm volatile("ds_read_b128 %0, %4 offset:" #OFF "\n\t"                                   \
+               "ds_read_b128 %1, %5 offset:" #OFF "\n\t"                                   \
+               "ds_read_b32 %2, %6 offset:" #OFF "\n\t"                                    \
+               "ds_read_b32 %3, %6 offset:" #OFF "+256\n\t"                                \
+               "s_waitcnt lgkmcnt(0)"                                                      \
+               : "=v"(u.lo), "=v"(u.hi), "=v"(u.sc), "=v"(u.s2)                            \
+               : "v"(a_lo), "v"(a_hi), "v"(a_sc)                                           \
+               : "memory")
+  auto read_slot = [&](auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    static_assert(kSlotBytes == 2560 && kSD == 2, "slot offsets below");
+    Staged u;
+    if constexpr (slot == 0) NF4_LN_READ(0);
+    else NF4_LN_READ(2560);
+    return u;
+  };
+#undef NF4_LN_READ
+
+  auto compute = [&](int ls, auto slot_c) {
+    const int xo = 256 * (s_begin + ls);
+    bf16x8_t afr[MH][8];
+#pragma unroll
+    for (int h = 0; h < MH; ++h)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) afr[h][t] = *reinterpret_cast<const bf16x8_t*>(xrow[h] + xo + 8 * t);
+    const Staged u = read_slot(slot_c);
+    float a;
+    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[u.sc & 0xFF], __uint_as_float(u.s2)), off);
+    else a = __uint_as_float(u.sc);
+    const Lut lt = make_lut(code, a);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint32_t o[4];
+      expand8_eo(t < 4 ? u.lo[t] : u.hi[t - 4], lt, o);
+      const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+#pragma unroll
+      for (int h = 0; h < MH; ++h)
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[h][t], bfr, acc[h], 0, 0, 0);
+    }
+  };
+  // Step ls reads slot ls % kSD; then the copy of step ls + kSD, if there is
+  // one, refills that slot.
+  auto one = [&](int ls, auto slot_c) {
+    constexpr int slot = decltype(slot_c)::value;
+    wait_copies(ls);
+    fence();
+    compute(ls, slot_c);
+    fence();
+    if (ls + kSD < nw) issue(ls + kSD, slot);
+    fence();
+  };
+  int s = 0;
+  for (; s + 2 <= nw; s += 2) {
+    one(s, ic<0>{});
+    one(s + 1, ic<1>{});
+  }
+  if (s < nw) one(s, ic<0>{});
+
+  // ---- fixed-order sum over the KW contraction slices of each row group ------
+  constexpr int kRegs = 4 * MH;
+  if constexpr (KW > 1) {
+    __syncthreads();                                   // x is no longer read
+    float* red = reinterpret_cast<float*>(xs);         // [KW-1][RW][regs][64]
+    if (kw > 0) {
+#pragma unroll
+      for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          red[(((kw - 1) * RW + rw) * kRegs + h * 4 + i) * 64 + lane] = acc[h][i];
+    }
+    __syncthreads();
+    if (kw > 0) return;
+    for (int v = 1; v < KW; ++v) {
+#pragma unroll
+      for (int h = 0; h < MH; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[h][i] = __fadd_rn(acc[h][i], red[(((v - 1) * RW + rw) * kRegs + h * 4 + i) * 64 + lane]);
+    }
+  }
+
+  // ---- epilogue: lane holds output column n, rows 16 h + 4 (lane / 16) + i ---
+  const int64_t n = rg0 + r;
+  if (n >= N) return;
+#pragma unroll
+  for (int h = 0; h < MH; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * h + 4 * g + i;
+      if (m >= M) continue;
+      if (p.splits == 1) {
+        p.y[static_cast<int64_t>(m) * N + n] = to_bf16(acc[h][i]);
+      } else {
+        p.partial[(static_cast<int64_t>(z) * M + m) * N + n] = acc[h][i];
+      }
+    }
+  }
+}
+
 // LDS of one launch: the x chunk (M + 1 rows) or the cross-wave sums, whichever is larger
 size_t gemv_region_bytes(int mp, int rw, int kw, int64_t M, int kc) {
   const size_t xb = static_cast<size_t>(M + 1) * static_cast<size_t>(kc + 8) * 2;
@@ -436,6 +758,41 @@ hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// the line-staged kernel: x region plus kSD staging slots per wave
+size_t gemv_ln_lds_bytes(int rw, int kw, int64_t M, int kc) {
+  return gemv_region_bytes(16, rw, kw, M, kc) + static_cast<size_t>(rw) * kw * kSD * kSlotBytes;
+}
+constexpr size_t kLnLdsMax = kXBudgetBytes + 4096 + kLnMaxWaves * kSD * kSlotBytes;
+
+template <int RW, int KW, bool NESTED, int MH>
+hipError_t launch_ln_t(const GemvParams& p, hipStream_t stream) {
+  auto kern = k_gemv_ln<RW, KW, NESTED, MH>;
+  static const bool attr_done = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLnLdsMax);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)attr_done;
+  const size_t need = gemv_ln_lds_bytes(RW, KW, p.M, p.kc);
+  const dim3 grid(static_cast<unsigned>((p.w.N + RW * 16 - 1) / (RW * 16)),
+                  static_cast<unsigned>(p.splits));
+  kern<<<grid, 64 * RW * KW, need, stream>>>(p);
+  return hipGetLastError();
+}
+
+template <int RW, bool NESTED, int MH>
+hipError_t launch_ln_kw(int kw, const GemvParams& p, hipStream_t stream) {
+  switch (kw) {
+    case 1: return launch_ln_t<RW, 1, NESTED, MH>(p, stream);
+    case 2: return launch_ln_t<RW, 2, NESTED, MH>(p, stream);
+    case 4: if constexpr (RW <= 2) return launch_ln_t<RW, 4, NESTED, MH>(p, stream); break;
+    case 8: if constexpr (RW == 1) return launch_ln_t<RW, 8, NESTED, MH>(p, stream); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int MP, int RW, bool NESTED, int MH>
 hipError_t launch_kw(int kw, const GemvParams& p, hipStream_t stream) {
   switch (kw) {
@@ -460,8 +817,11 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   // 109 vs 130 us at M = 17, 119 vs 130 us at M = 24, but 143 vs 136 us at
   // M = 32, where the halves' smaller x chunks cost more partial traffic);
   // tuning override (documented): NF4_GEMV_MP32=0/1 picks either above M = 16
+  // (above M = 16 the 32-row groups win on the large projections: at M = 24
+  // the forward of gate 21.9 vs 31.4 us, at M = 32 q 14.6 vs 16.5 us, while
+  // the 16-row kernel keeps k / v at 9.0 vs 12.9 us at M = 24)
   const char* o32 = getenv("NF4_GEMV_MP32");
-  bool mp32 = M > 24;
+  bool mp32 = M > 24 || (M > 16 && N * K >= (int64_t{32} << 20));
   if (o32 && (o32[0] == '0' || o32[0] == '1')) mp32 = o32[0] == '1';
   pl.bm = (M > 16 && mp32) ? 32 : 16;
   const int step = pl.bm == 16 ? 256 : 128;
@@ -477,35 +837,47 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   kc = (kc + step - 1) / step * step;
   z = (K + kc - 1) / kc;
   const int64_t steps = kc / step;
-  // Row groups per workgroup: each shares one staged x chunk.  At M <= 4 the
-  // chunk is two rows and one group is best; above, the largest of 4 / 2 / 1
-  // groups that still gives 1.5 workgroups per compute unit (measured: 4
-  // groups take the gate projection at M = 16 from 24.8 to 19.9 us, but slow
-  // the q projection, which then has too few workgroups); 32-row groups: 4.
+  // Row groups per workgroup: each shares one staged x chunk.  32-row groups:
+  // 4.  16-row groups (line-staged kernel): 4 above M = 4 when there are
+  // still as many such workgroups as compute units (half as many above
+  // M = 8), else 1; contraction
+  // slices per row group: 2 with four row groups (8 waves), otherwise the
+  // power of two (at most 8) that brings the launch to about 2048 waves.
+  // Measured over the Llama-3.1-8B projections: at M = 8 four row groups take
+  // the forward of gate / down from 18.2 / 24.1 to 16.9 / 16.5 us, while q and
+  // k are best with one row group and 8 slices (9.9 / 7.4 us); at M = 1 the
+  // slices give gate 13.1 (4 slices), q 7.1 and k 5.9 us (8 slices).
   int rw = 1;
+  int kw = 1;
+  const int64_t rg16 = (N + 15) / 16;
   if (pl.bm == 32) {
     rw = 4;
-  } else if (M > 4) {
-    for (int c = 4; c >= 1; c /= 2) {
-      const int64_t wgs_c = (N + 16 * c - 1) / (16 * c) * z;
-      if (2 * wgs_c >= 3 * static_cast<int64_t>(cus) || c == 1) { rw = c; break; }
+    // 32-row groups (streaming kernel with per-lane block loads): 2 slices,
+    // doubled while a slice would hold more than 16 steps
+    kw = 2;
+    while (kw < 8 && steps > 16 * kw) kw *= 2;
+  } else {
+    // (at M = 16 the forward of q takes 11.2 us with four row groups, 15.3
+    // with one; at M = 8 one row group and 8 slices are best for it, 9.9 us)
+    const int64_t wgs4 = (rg16 + 3) / 4 * z;
+    if (M > 4 && (wgs4 >= cus || (M > 8 && 2 * wgs4 >= cus))) rw = 4;
+    if (rw == 4) {
+      kw = 2;
+    } else {
+      const int64_t wgs = rg16 * z;
+      while (kw < 8 && wgs * kw < 2048) kw *= 2;
     }
   }
   // tuning override (documented): NF4_GEMV_RW (row groups per workgroup: 1 / 2 / 4 at M <= 16)
   const char* orw = getenv("NF4_GEMV_RW");
   if (orw && pl.bm == 16 && (atoi(orw) == 1 || atoi(orw) == 2 || atoi(orw) == 4)) rw = atoi(orw);
   pl.bn = rw;
-  // contraction slices per row group: 4 with one row group, else 2, doubled
-  // while a slice would hold more than 8 steps.  Workgroups of 4-8 waves keep
-  // two or more workgroups on a compute unit, so one workgroup's prologue and
-  // cross-wave sum overlap another's expansion (16-wave workgroups measured up
-  // to 2.4x slower at the same work).
-  // (two x halves hold twice the accumulators: at most 8 waves per group)
-  const int kw_max = (pl.bm == 16 && M > 16 ? kMaxWaves / 2 : kMaxWaves) / rw;
-  int kw = rw == 1 ? 4 : 2;
-  while (kw < 8 && kw < kw_max && steps > 8 * kw) kw *= 2;
+  // the line-staged kernel holds two staging slots per wave: at most
+  // kLnMaxWaves waves per workgroup; 32-row groups: 16
+  const int kw_max = (pl.bm == 16 ? kLnMaxWaves : kMaxWaves) / rw;
+  if (kw > kw_max) kw = kw_max;
   while (kw > 1 && kw > steps) kw /= 2;         // no idle slices on short contractions
-  // tuning override (documented): NF4_GEMV_KW (1, 2, 4, 8, 16 within kMaxWaves / RW)
+  // tuning override (documented): NF4_GEMV_KW (1, 2, 4, 8 (16 with 32-row groups) within the waves cap / RW)
   const char* okw = getenv("NF4_GEMV_KW");
   if (okw) {
     const int v = atoi(okw);
@@ -529,25 +901,28 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   p.M = static_cast<int32_t>(M);
   p.splits = plan.splits;
   p.kc = plan.kc;
+  const bool nested = w.nested();
+  const int kw = plan.consumers;
+  if (plan.bm == 16) {
+    // line-staged kernel; two halves of x per expanded fragment above M = 16
+    if (plan.bn * kw > kLnMaxWaves || gemv_ln_lds_bytes(plan.bn, kw, M, plan.kc) > kLnLdsMax)
+      return hipErrorInvalidValue;
+    p.tb_off = static_cast<int32_t>(gemv_region_bytes(16, plan.bn, kw, M, plan.kc));
+    if (M > 16) {
+      if (plan.bn == 1) return nested ? launch_ln_kw<1, true, 2>(kw, p, stream) : launch_ln_kw<1, false, 2>(kw, p, stream);
+      if (plan.bn == 2) return nested ? launch_ln_kw<2, true, 2>(kw, p, stream) : launch_ln_kw<2, false, 2>(kw, p, stream);
+      if (plan.bn == 4) return nested ? launch_ln_kw<4, true, 2>(kw, p, stream) : launch_ln_kw<4, false, 2>(kw, p, stream);
+      return hipErrorInvalidValue;
+    }
+    if (plan.bn == 1) return nested ? launch_ln_kw<1, true, 1>(kw, p, stream) : launch_ln_kw<1, false, 1>(kw, p, stream);
+    if (plan.bn == 2) return nested ? launch_ln_kw<2, true, 1>(kw, p, stream) : launch_ln_kw<2, false, 1>(kw, p, stream);
+    if (plan.bn == 4) return nested ? launch_ln_kw<4, true, 1>(kw, p, stream) : launch_ln_kw<4, false, 1>(kw, p, stream);
+    return hipErrorInvalidValue;
+  }
   if (gemv_lds_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc) >
       static_cast<size_t>(kXBudgetBytes + 4096 + kMaxWaves * kTBufBytes))
     return hipErrorInvalidValue;
   p.tb_off = static_cast<int32_t>(gemv_region_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc));
-  const bool nested = w.nested();
-  const int kw = plan.consumers;
-  if (plan.bm == 16 && M > 16) {
-    // 16-row groups, two halves of x per expanded fragment
-    if (plan.bn == 1) return nested ? launch_kw<16, 1, true, 2>(kw, p, stream) : launch_kw<16, 1, false, 2>(kw, p, stream);
-    if (plan.bn == 2) return nested ? launch_kw<16, 2, true, 2>(kw, p, stream) : launch_kw<16, 2, false, 2>(kw, p, stream);
-    if (plan.bn == 4) return nested ? launch_kw<16, 4, true, 2>(kw, p, stream) : launch_kw<16, 4, false, 2>(kw, p, stream);
-    return hipErrorInvalidValue;
-  }
-  if (plan.bm == 16) {
-    if (plan.bn == 1) return nested ? launch_kw<16, 1, true, 1>(kw, p, stream) : launch_kw<16, 1, false, 1>(kw, p, stream);
-    if (plan.bn == 2) return nested ? launch_kw<16, 2, true, 1>(kw, p, stream) : launch_kw<16, 2, false, 1>(kw, p, stream);
-    if (plan.bn == 4) return nested ? launch_kw<16, 4, true, 1>(kw, p, stream) : launch_kw<16, 4, false, 1>(kw, p, stream);
-    return hipErrorInvalidValue;
-  }
   if (plan.bn == 4) return nested ? launch_kw<32, 4, true, 1>(kw, p, stream) : launch_kw<32, 4, false, 1>(kw, p, stream);
   return hipErrorInvalidValue;
 }

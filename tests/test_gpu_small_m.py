@@ -161,3 +161,29 @@ def test_small_m_slices_and_chunks(M, rw, mp32, kw, z):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not bitwise repeatable"
     assert_close(y, O.matmul_fwd(xb, wb), f"y M={M} rw={rw} mp32={mp32} kw={kw} z={z}",
                  O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+
+
+@pytest.mark.parametrize("kw", ["2", "4"])
+@pytest.mark.parametrize("N,K", [(136, 320), (144, 512), (144, 320)])
+def test_small_m_one_step_waves_repeat(N, K, kw):
+    """Contraction slices of one step each (and empty ones), nested scales:
+    thirty calls in a row are bitwise equal and match the oracle.  (Covers the
+    stale reads a wave once got when a repeat copy of the lines it waited for
+    was still in flight.)"""
+    M = 2
+    wq, wb, x = _setup(M, N, K, True, M + N + K)
+    want = O.matmul_fwd(WL.bf16_bits(x), wb)
+    old = os.environ.get("NF4_GEMV_KW")
+    os.environ["NF4_GEMV_KW"] = kw
+    try:
+        xd = x.to(DEV)
+        ys = [api.nf4_matmul_fwd(xd, wq) for _ in range(30)]
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            os.environ.pop("NF4_GEMV_KW", None)
+        else:
+            os.environ["NF4_GEMV_KW"] = old
+    for i, y in enumerate(ys):
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16)), f"call {i} differs"
+    assert_close(ys[0], want, f"y {M}x{N}x{K} kw={kw}")
