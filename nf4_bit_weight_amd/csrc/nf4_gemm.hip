@@ -141,6 +141,33 @@ __device__ __forceinline__ int xcd_tile(int L, int T) {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
+// LDS-direct copies written as inline assembly.  The compiler's own wait
+// insertion treats every LDS access that may alias a pending LDS-direct copy
+// as needing vmcnt(0); with the copies issued through the builtins it put
+// about five such waits into each step of the ping-pong kernel (before the
+// expanded-tile stores and the fragment reads), so every copy was waited for
+// right after it was issued.  Copies issued here are invisible to it; the
+// kernel's explicit waits (also assembly, vm_wait below) are then the only
+// waits on them.  The wave-uniform LDS address is passed in M0; one wait
+// state separates the M0 write from the copy.
+__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma_u8(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_ubyte %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+template <int C>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(C >= 0 && C < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(C) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void_t*)p));
+}
+
 // Rows of row tile mt: [row0, row_end) of A and C, and the first row of the
 // weight tensor it multiplies.  Dense: tile mt of BM rows.  Grouped: the row
 // tiles are numbered expert by expert (ceil(rows_e / BM) tiles each, from the
@@ -626,6 +653,7 @@ struct PP {
   // kernel's LDS cycles).
   static constexpr int kBTPitch = BN;
   static constexpr int kWSlot = 10240;          // 8 KB packed, 1 KB scales, 1 KB nested scales
+  static constexpr int kWSlots = 3;             // weight slots: each copy has two steps to land
   // unit swizzle of row r: rows r & 3 = 0..3 take distinct bits 2-3 (reads
   // of four rows), and over r & 7 the values with bit 2 cleared are distinct
   // (writes of eight rows, two halves 4 units apart)
@@ -633,7 +661,7 @@ struct PP {
   template <bool TRANS>
   static constexpr int b_elems() { return TRANS ? BK * kBTPitch : BN * BK; }
   template <bool TRANS>
-  static constexpr int lds_bytes() { return 2 * kAElems * 2 + 2 * b_elems<TRANS>() * 2 + 2 * kWSlot; }
+  static constexpr int lds_bytes() { return 2 * kAElems * 2 + 2 * b_elems<TRANS>() * 2 + kWSlots * kWSlot; }
 };
 static_assert(PP::lds_bytes<true>() + 1024 <= 160 * 1024, "LDS budget of one workgroup");
 
@@ -699,7 +727,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     int64_t col = c0 + a_colofs[j];
     col = col < Kc ? col : Kc - 8;
     const uint16_t* src = a_row_ptr[j] + col;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(a_tile(stage) + (32 * wave + 8 * j) * BK), 16, 0, 0);
+    dma_b128(src, __builtin_amdgcn_readfirstlane(lds_addr(a_tile(stage) + (32 * wave + 8 * j) * BK)));
   };
   // weights: thread t expands half h = t & 1 of unit u = t >> 1 of the step
   // (fwd: W row col0 + u, block kt; bwd: W row kt*64 + u % 64, block
@@ -744,7 +772,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     const int kt = kb + (i < n ? i : n - 1);
     char* sl = w_area + slot * PP::kWSlot;
     const uint8_t* src = unit_valid(own, kt) ? pk_base + ((static_cast<int64_t>(kt) * dstep) >> 1) : p.w.packed;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sl + 1024 * wave), 16, 0, 0);
+    dma_b128(src, __builtin_amdgcn_readfirstlane(lds_addr(sl + 1024 * wave)));
   };
   auto issue_ws = [&](int i, int slot) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
@@ -753,15 +781,15 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     if (wave < 4) {
       if constexpr (NESTED) {
         // one byte per lane, written zero-extended to the lane's dword
-        __builtin_amdgcn_global_load_lds(static_cast<const uint8_t*>(p.w.absmax) + b,
-                                         (lds_void_t*)(sl + 8192 + 256 * wave), 1, 0, 0);
+        dma_u8(static_cast<const uint8_t*>(p.w.absmax) + b,
+               __builtin_amdgcn_readfirstlane(lds_addr(sl + 8192 + 256 * wave)));
       } else {
-        __builtin_amdgcn_global_load_lds(static_cast<const float*>(p.w.absmax) + b,
-                                         (lds_void_t*)(sl + 8192 + 256 * wave), 4, 0, 0);
+        dma_b32(static_cast<const float*>(p.w.absmax) + b,
+                __builtin_amdgcn_readfirstlane(lds_addr(sl + 8192 + 256 * wave)));
       }
     } else if constexpr (NESTED) {
-      __builtin_amdgcn_global_load_lds(p.w.nested_absmax + (b >> 8),
-                                       (lds_void_t*)(sl + 9216 + 256 * (wave - 4)), 4, 0, 0);
+      dma_b32(p.w.nested_absmax + (b >> 8),
+              __builtin_amdgcn_readfirstlane(lds_addr(sl + 9216 + 256 * (wave - 4))));
     }
   };
   const uint32_t st_pk = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)w_area)) + 16 * tid;
@@ -781,9 +809,10 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
                : "memory")
   auto read_unit = [&](int slot) __attribute__((always_inline)) {
     Staged r;
-    static_assert(PP::kWSlot == 10240, "slot offsets below");
+    static_assert(PP::kWSlot == 10240 && PP::kWSlots == 3, "slot offsets below");
     if (slot == 0) NF4_PP_READ(0);
-    else NF4_PP_READ(10240);
+    else if (slot == 1) NF4_PP_READ(10240);
+    else NF4_PP_READ(20480);
     return r;
   };
 #undef NF4_PP_READ
@@ -795,14 +824,19 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       return b_tile(buf) + u * BK + 8 * swz(u, 4 * hh + d);
     }
   };
-  // the copies of step `ci` issued from inside the first phase of a step:
-  // group g of that phase issues activation copy g, plus the weight copy
-  // (g == 1) and the scale copy (g == 2)
+  // The copies issued from inside the first phase of step ci: group g issues
+  // activation copy g of step ci + 1, and after the last one (g == 3) the
+  // packed-weight and scale copies of step ci + 3 into slot ci % 3 (the
+  // slot of step ci, expanded in step ci - 1).  Copies of steps past the end
+  // are not issued: a second copy of lines already in flight could let the
+  // counted wait below pass before the first one has landed.
   int ci = 0;
   auto dma = [&](int g) __attribute__((always_inline)) {
-    issue_a(ci + 1, (ci + 1) & 1, g);
-    if (g == 1) issue_wpk(ci + 2, ci & 1);
-    if (g == 2) issue_ws(ci + 2, ci & 1);
+    if (ci + 1 < n) issue_a(ci + 1, (ci + 1) & 1, g);
+    if (g == 3 && ci + 3 < n) {
+      issue_wpk(ci + 3, ci % 3);
+      issue_ws(ci + 3, ci % 3);
+    }
   };
   auto expand = [&](int i, int slot, int buf, bool with_dma) __attribute__((always_inline)) {
     const int kt = kb + (i < n ? i : n - 1);
@@ -871,21 +905,39 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     bf16x8_t a[PP::MI];
     bf16x8_t b[PP::NI];
   };
+  // The transposed reads are one assembly block that waits for its own data:
+  // issued through the builtin, each one was preceded by a compiler-inserted
+  // vmcnt(0), which waited for the step's copies right after their issue.
+  static_assert(!TRANS || PP::NI == 2, "four transposed reads per slice");
+  uint32_t tr_addr[2][2];
+  if constexpr (TRANS) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) tr_addr[j][hf] = lds_addr(pbt[j][hf]);
+  }
   auto load_frags = [&](int stage, int buf, int kk, Frags& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PP::MI; ++i)
       f.a[i] = *reinterpret_cast<const bf16x8_t*>(pa[kk & 3] + stage * PP::kAElems * 2 + i * 32 * BK * 2);
+    if constexpr (TRANS) {
+      const uint32_t off = static_cast<uint32_t>((buf * kBElems + 16 * kk * PP::kBTPitch) * 2);
+      u32x2_t l0, h0, l1, h1;
+      asm volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                   "ds_read_b64_tr_b16 %1, %5\n\t"
+                   "ds_read_b64_tr_b16 %2, %6\n\t"
+                   "ds_read_b64_tr_b16 %3, %7\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1)
+                   : "v"(tr_addr[0][0] + off), "v"(tr_addr[0][1] + off), "v"(tr_addr[1][0] + off),
+                     "v"(tr_addr[1][1] + off)
+                   : "memory");
+      f.b[0] = __builtin_bit_cast(bf16x8_t, u32x4_t{l0[0], l0[1], h0[0], h0[1]});
+      f.b[1] = __builtin_bit_cast(bf16x8_t, u32x4_t{l1[0], l1[1], h1[0], h1[1]});
+    } else {
 #pragma unroll
-    for (int j = 0; j < PP::NI; ++j) {
-      if constexpr (TRANS) {
-        const int off = (buf * kBElems + 16 * kk * PP::kBTPitch) * 2;
-        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pbt[j][0] + off));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(pbt[j][1] + off));
-        u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
-        f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
-      } else {
+      for (int j = 0; j < PP::NI; ++j)
         f.b[j] = *reinterpret_cast<const bf16x8_t*>(pb[kk & 3] + buf * kBElems * 2 + j * 32 * BK * 2);
-      }
     }
   };
   // slice 0 of a step's fragments is read ahead, right after the barrier
@@ -960,18 +1012,30 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   };
 
   // ---- pipeline -------------------------------------------------------------------
-  // Step i multiplies stage/buffer i % 2 and expands step i+1 into the other
-  // buffer.  At its start every wave issues the activation copy of step i+1
-  // and the weight copy of step i+2; all of them must have landed by the end
-  // of the step (vmcnt(0)), then one barrier.
+  // Step i multiplies stage/buffer i % 2 and expands step i+1 (slot
+  // (i+1) % 3) into the other buffer.  During its first phase every wave
+  // issues the activation copy of step i+1, then the weight copies of step
+  // i+3.  By the end of the step the activation copy must have landed, and
+  // so have the weights of step i+2 (issued one step earlier, so older than
+  // that activation copy); the weight copies of step i+3 (kWc per wave, the
+  // newest) may stay in flight.  Then one barrier.
+  // (assembly: the copies are invisible to the compiler's wait bookkeeping)
   auto wait_vm = [](auto cnt) {
-    constexpr int c = decltype(cnt)::value;
-    __builtin_amdgcn_s_waitcnt((c & 15) | ((c >> 4) << 14) | (7 << 4));
+    vm_wait<decltype(cnt)::value>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  auto end_step = [&]() {
+  // weight copies per wave and step: packed bytes, plus a scale (waves 0-3)
+  // or a nested scale (waves 4-7, nested form only)
+  const bool two_w = wave < 4 || NESTED;
+  auto end_step = [&](int i) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    wait_vm(ic<0>{});
+    if (i + 3 < n) {
+      if (two_w) wait_vm(ic<2>{});
+      else wait_vm(ic<1>{});
+    } else {
+      wait_vm(ic<0>{});
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -983,9 +1047,18 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
     for (int j = 0; j < 4; ++j) issue_a(0, 0, j);
     issue_wpk(0, 0);
     issue_ws(0, 0);
-    issue_wpk(1, 1);
-    issue_ws(1, 1);
-    wait_vm(ic<0>{});
+    if (n > 1) {
+      issue_wpk(1, 1);
+      issue_ws(1, 1);
+    }
+    if (n > 2) {
+      issue_wpk(2, 2);
+      issue_ws(2, 2);
+      if (two_w) wait_vm(ic<2>{});                // all but the weights of step 2
+      else wait_vm(ic<1>{});
+    } else {
+      wait_vm(ic<0>{});
+    }
     __syncthreads();                               // every wave's copies of steps 0 and 1 landed
     expand(0, 0, 0, false);
     __syncthreads();
@@ -994,18 +1067,18 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
       constexpr int P = decltype(ph)::value;
       ci = i;
       if constexpr (!TRANS) {
-        mixed(i, P & 1, P & 1, (P + 1) & 1, (P + 1) & 1);
+        mixed(i, P & 1, P & 1, (i + 1) % 3, (P + 1) & 1);
       } else {
         // the input gradient measured faster with the two halves of a step
         // run as separate phases, in opposite order on the two waves of a
         // SIMD (w and w + 4): one wave's expansion under the other's MFMAs
-        if (!mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, true);
+        if (!mfma_first) expand(i + 1, (i + 1) % 3, (P + 1) & 1, true);
         __builtin_amdgcn_sched_barrier(0);
         compute(P & 1, P & 1, mfma_first);
         __builtin_amdgcn_sched_barrier(0);
-        if (mfma_first) expand(i + 1, (P + 1) & 1, (P + 1) & 1, false);
+        if (mfma_first) expand(i + 1, (i + 1) % 3, (P + 1) & 1, false);
       }
-      end_step();
+      end_step(i);
       // slice 0 of step i+1 (a harmless re-read of landed data after the last step)
       if constexpr (TRANS) load_frags((P + 1) & 1, (P + 1) & 1, 0, fpre);
     };

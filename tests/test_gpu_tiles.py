@@ -121,10 +121,14 @@ def test_register_operand_forward_repeats_bitwise(bn, plan_override):
 # activation stages, 2 or 4 packed-weight slots, by tile and direction) repeat
 # with a period of 4 steps, and its step loop is unrolled by 4.
 RING_TILES = [(256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1), (128, 128, 1), (64, 128, 1)]
+# The ping-pong kernel (256 x 256, consumers 4; with 0 the input gradient
+# only): its weight copies run three steps ahead through three slots, and the
+# last steps issue no copies, so its short contractions need the same sweep.
+PP_TILES = [(256, 256, 4), (256, 256, 0)]
 
 
 @pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 10, 11, 13])
-@pytest.mark.parametrize("bm,bn,consumers", RING_TILES)
+@pytest.mark.parametrize("bm,bn,consumers", RING_TILES + PP_TILES)
 def test_tiled_step_counts(steps, bm, bn, consumers, plan_override):
     """One workgroup's contraction of 1 to 13 steps in both directions: every
     remainder of the unrolled step loop with and without a whole period, and
