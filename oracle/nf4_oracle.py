@@ -50,6 +50,9 @@ R8  Matmul reference: the exact product of the bf16 operands, accumulated in
     fp64 (a library matmul is the step).  The fused kernel sums in another
     order, so the GEMM comparison is a tolerance, the codec comparison is
     bit-exact.
+R9  8-bit maps (int8 "dynamic map", fp8 e4m3 codebook): not defined on the
+    pages; an ascending 256-entry fp32 table passed in.
+R10 8-bit packing: one index per byte, in element order.
 """
 
 from __future__ import annotations
@@ -314,11 +317,68 @@ def grouped_matmul_bwd_input(gy_bf16_bits: np.ndarray, offsets: np.ndarray,
     return out
 
 
+# ---- 8-bit blockwise variants --------------------------------------------------
+# bitsandbytes fork PR "Experts trainability ... ExpertsNbit", "Commit 1": its
+# quant_type table lists 8-bit blockwise formats (int8 with a dynamic map, fp8
+# e4m3 with its codebook) beside nf4 / fp4: one byte per weight, the same
+# 64-element blocks and absmax (optionally double-quantised).  The pages do
+# not define either 256-entry map, so (R9) the map is an explicit ascending
+# 256-entry table passed in, exactly like the 16-entry NF4 code: the index is
+# found by R4, one index per byte (R10), and the decode is R7 with this table.
+
+def nearest_index_sorted(t: np.ndarray, mids: np.ndarray) -> np.ndarray:
+    """Number of midpoints strictly below each t (R4), for midpoints in
+    ascending order: the position of the first midpoint that is >= t, found
+    by a sorted search (the library step; equal to the count of
+    nearest_index)."""
+    return np.searchsorted(np.asarray(mids, dtype=F32), np.asarray(t, dtype=F32), side="left")
+
+
+def quantize_blockwise8(w: np.ndarray, code: np.ndarray, nested_code: np.ndarray | None = None,
+                        nested: bool = False) -> dict:
+    """8-bit blockwise quantisation of W (flattened row-major) with a
+    256-entry ascending table: steps 1-3 and 5 of quantize_nf4, one index per
+    byte in element order (R10).  Returns the same fields, packed u8[n]."""
+    code = np.asarray(code, dtype=F32)
+    if code.shape != (256,):
+        raise ValueError("the 8-bit formats take a 256-entry table")
+    flat = np.ascontiguousarray(w, dtype=F32).reshape(-1)
+    absmax = _blockwise_absmax(flat, BLOCK).astype(F32)
+    t = _scale_to_unit(flat, absmax, BLOCK)
+    packed = nearest_index_sorted(t, midpoints(code)).astype(np.uint8)
+    if not nested:
+        return dict(packed=packed, absmax=absmax, nested_absmax=None, nested_offset=None)
+    ncode = uniform_nested_code() if nested_code is None else np.asarray(nested_code, dtype=F32)
+    offset = absmax_mean_offset(absmax)
+    c = (absmax - offset).astype(F32)
+    s2 = _blockwise_absmax(c, NESTED_BLOCK).astype(F32)
+    t2 = _scale_to_unit(c, s2, NESTED_BLOCK)
+    q2 = nearest_index(t2, midpoints(ncode)).astype(np.uint8)
+    return dict(packed=packed, absmax=q2, nested_absmax=s2, nested_offset=F32(offset))
+
+
+def dequantize_blockwise8_f32(packed: np.ndarray, absmax: np.ndarray, nested_absmax=None,
+                              nested_offset=None, code=None, nested_code=None) -> np.ndarray:
+    """w_hat = fp32(code[q] * absmax_hat[block]) with one byte per index (R7, R10)."""
+    code = np.asarray(code, dtype=F32)
+    q = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    scale = decode_absmax(absmax, nested_absmax, nested_offset, nested_code)
+    blk = np.arange(q.shape[0]) // BLOCK
+    return (code[q] * scale[blk]).astype(F32)
+
+
+def dequantize_blockwise8_bf16_bits(packed, absmax, nested_absmax=None, nested_offset=None,
+                                    code=None, nested_code=None) -> np.ndarray:
+    """The 8-bit dequantised weight in the compute dtype (bf16 bits)."""
+    return bf16_rne_bits(dequantize_blockwise8_f32(packed, absmax, nested_absmax, nested_offset,
+                                                   code, nested_code))
+
+
 # ---- storage accounting (bytes per format) ----------------------------------
 
-def packed_bytes(n_elems: int) -> int:
-    """Two 4-bit values per byte (Experts PR "Commit 1" table)."""
-    return n_elems // 2
+def packed_bytes(n_elems: int, bits: int = 4) -> int:
+    """Two 4-bit values per byte, or one 8-bit value (Experts PR "Commit 1" table)."""
+    return n_elems // 2 if bits == 4 else n_elems
 
 
 def absmax_count(n_elems: int) -> int:
@@ -329,9 +389,9 @@ def nested_count(n_elems: int) -> int:
     return -(-absmax_count(n_elems) // NESTED_BLOCK)
 
 
-def storage_bytes(n_elems: int, nested: bool) -> int:
+def storage_bytes(n_elems: int, nested: bool, bits: int = 4) -> int:
     """Bytes of packed data + statistics for one quantised tensor."""
     nb = absmax_count(n_elems)
     if nested:
-        return packed_bytes(n_elems) + nb + 4 * nested_count(n_elems) + 4
-    return packed_bytes(n_elems) + 4 * nb
+        return packed_bytes(n_elems, bits) + nb + 4 * nested_count(n_elems) + 4
+    return packed_bytes(n_elems, bits) + 4 * nb

@@ -78,6 +78,30 @@ FP4_LEVELS = (
 )
 
 
+def int8_code_np() -> np.ndarray:
+    """The 8-bit integer map (a call argument): index j stands for the signed
+    integer j - 128 scaled by 1/127, so |t| <= 1 uses indices 1 .. 255 and
+    the block's absmax element maps to +-127 exactly."""
+    j = np.arange(256, dtype=np.float64)
+    return ((j - 128.0) / 127.0).astype(np.float32)
+
+
+def fp8_e4m3_code_np() -> np.ndarray:
+    """The fp8 e4m3 codebook (a call argument): the values of all 256 bit
+    patterns of a float with 1 sign, 4 exponent (bias 7) and 3 mantissa bits,
+    exponent field 0 subnormal, every pattern finite (largest 1.875 * 2^8 =
+    480), divided by 480 so the largest is 1, in ascending order with -0
+    before +0.  The stored byte is the rank in this table."""
+    vals = []
+    for bits in range(256):
+        sign = -1.0 if bits & 0x80 else 1.0
+        e, m = (bits >> 3) & 15, bits & 7
+        mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+        vals.append((sign * mag, 0 if bits & 0x80 else 1))
+    vals.sort()
+    return np.array([v / 480.0 for v, _ in vals], dtype=np.float64).astype(np.float32)
+
+
 def nf4_code_np() -> np.ndarray:
     return np.array(NF4_LEVELS, dtype=np.float64).astype(np.float32)
 
