@@ -104,6 +104,8 @@ extern "C" {
 #define NF4_OP_MATMUL_BWD_INPUT  2
 #define NF4_OP_GROUPED_FWD       3
 #define NF4_OP_GROUPED_BWD_INPUT 4
+#define NF4_OP_MATMUL_FWD_8BIT        5
+#define NF4_OP_MATMUL_BWD_INPUT_8BIT  6
 
 /* ---- path counters (host-side launch counts; they prove which kernel ran,
  *      as the "Acceptance criteria" of Soup issue #842 ask) ---------------- */
@@ -115,7 +117,9 @@ extern "C" {
 #define NF4_PATH_SPLITK_REDUCE  5  /* fixed-order reduction of split partials   */
 #define NF4_PATH_GROUPED_FWD    6  /* grouped (expert) forward                  */
 #define NF4_PATH_GROUPED_BWD    7  /* grouped (expert) input gradient           */
-#define NF4_PATH_COUNT          8
+#define NF4_PATH_FWD_8BIT       8  /* 8-bit blockwise forward (plain or grouped) */
+#define NF4_PATH_BWD_8BIT       9  /* 8-bit blockwise input gradient            */
+#define NF4_PATH_COUNT         10
 
 /*
  * nf4_quantize -- NF4 blockwise quantisation of w [N, K] (bitsandbytes #2034,
@@ -213,6 +217,61 @@ int nf4_grouped_matmul_bwd_input(const void* grad_y, const int32_t* offsets,
                                  const float* code16, const float* nested_code256,
                                  int64_t N, int64_t K, void* grad_x, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/*
+ * ---- 8-bit blockwise variants --------------------------------------------
+ * bitsandbytes fork PR "Experts trainability: bit-exact recompute-in-backward
+ * + ExpertsNbit", "Commit 1": its quant_type table lists 8-bit blockwise
+ * formats (int8 with a dynamic map, fp8 e4m3 with its codebook) beside nf4
+ * and fp4.  Same blocks of 64, same plain or nested absmax, but one byte per
+ * weight: the byte is an index into an ascending 256-entry fp32 table
+ * `code256` passed in (the pages define neither map; any ascending table
+ * works, for example the integers -128..127 over 127 or the e4m3 values over
+ * their largest).  Encoding: index = number of table midpoints strictly
+ * below t = fp32(w / absmax) (the 4-bit rule with 255 midpoints); decode
+ * w_hat = bf16_rne(fp32(code256[q] * absmax_hat)).
+ * W8-args: (packed u8[N*K], absmax, nested_absmax, nested_offset, code256,
+ * nested_code256, N, K); the statistics fields are as for the 4-bit form.
+ * Conventions (memory, streams, errors, determinism) as above.  The matmuls
+ * run their own fused kernel (path counters NF4_PATH_FWD_8BIT /
+ * NF4_PATH_BWD_8BIT), workspace from NF4_OP_MATMUL_FWD_8BIT /
+ * NF4_OP_MATMUL_BWD_INPUT_8BIT; the grouped calls need none.
+ */
+int nf4_quantize_8bit(const void* w, int w_dtype, int64_t N, int64_t K,
+                      const float* code256, const float* nested_code256,
+                      uint8_t* packed, void* absmax, float* nested_absmax,
+                      float* nested_offset, void* ws, size_t ws_bytes, void* stream);
+int nf4_dequantize_8bit(const uint8_t* packed, const void* absmax,
+                        const float* nested_absmax, const float* nested_offset,
+                        const float* code256, const float* nested_code256,
+                        int64_t N, int64_t K, int out_dtype, void* out, void* stream);
+int nf4_matmul_fwd_8bit(const void* x, int64_t M,
+                        const uint8_t* packed, const void* absmax,
+                        const float* nested_absmax, const float* nested_offset,
+                        const float* code256, const float* nested_code256,
+                        int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes,
+                        void* stream);
+int nf4_matmul_bwd_input_8bit(const void* grad_y, int64_t M,
+                              const uint8_t* packed, const void* absmax,
+                              const float* nested_absmax, const float* nested_offset,
+                              const float* code256, const float* nested_code256,
+                              int64_t N, int64_t K, void* grad_x, void* ws,
+                              size_t ws_bytes, void* stream);
+int nf4_grouped_matmul_fwd_8bit(const void* x, const int32_t* offsets, int32_t E,
+                                int64_t total_M,
+                                const uint8_t* packed, const void* absmax,
+                                const float* nested_absmax, const float* nested_offset,
+                                const float* code256, const float* nested_code256,
+                                int64_t N, int64_t K, void* y, void* ws,
+                                size_t ws_bytes, void* stream);
+int nf4_grouped_matmul_bwd_input_8bit(const void* grad_y, const int32_t* offsets,
+                                      int32_t E, int64_t total_M,
+                                      const uint8_t* packed, const void* absmax,
+                                      const float* nested_absmax,
+                                      const float* nested_offset,
+                                      const float* code256, const float* nested_code256,
+                                      int64_t N, int64_t K, void* grad_x, void* ws,
+                                      size_t ws_bytes, void* stream);
 
 /*
  * nf4_matmul_fwd_noalloc -- nf4_matmul_fwd without a workspace argument, for

@@ -34,9 +34,11 @@ NF4_OP_MATMUL_FWD = 1
 NF4_OP_MATMUL_BWD_INPUT = 2
 NF4_OP_GROUPED_FWD = 3
 NF4_OP_GROUPED_BWD_INPUT = 4
+NF4_OP_MATMUL_FWD_8BIT = 5
+NF4_OP_MATMUL_BWD_INPUT_8BIT = 6
 
 PATHS = ("quantize", "dequantize", "fwd_tiled", "fwd_small_m", "bwd_tiled",
-         "splitk_reduce", "grouped_fwd", "grouped_bwd")
+         "splitk_reduce", "grouped_fwd", "grouped_bwd", "fwd_8bit", "bwd_8bit")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -53,6 +55,12 @@ SIGNATURES = {
     "nf4_matmul_fwd": (_int, [_vp, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_matmul_bwd_input": (_int, [_vp, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_matmul_fwd_noalloc": (_int, [_vp, _i64, *_W, _vp, _vp]),
+    "nf4_quantize_8bit": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size, _vp]),
+    "nf4_dequantize_8bit": (_int, [*_W, _int, _vp, _vp]),
+    "nf4_matmul_fwd_8bit": (_int, [_vp, _i64, *_W, _vp, _vp, _size, _vp]),
+    "nf4_matmul_bwd_input_8bit": (_int, [_vp, _i64, *_W, _vp, _vp, _size, _vp]),
+    "nf4_grouped_matmul_fwd_8bit": (_int, [_vp, _vp, _i32, _i64, *_W, _vp, _vp, _size, _vp]),
+    "nf4_grouped_matmul_bwd_input_8bit": (_int, [_vp, _vp, _i32, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_grouped_matmul_fwd": (_int, [_vp, _vp, _i32, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_grouped_matmul_bwd_input": (_int, [_vp, _vp, _i32, _i64, *_W, _vp, _vp, _size, _vp]),
     "nf4_workspace_bytes": (_size, [_int, _i64, _i64, _i64, _i32]),

@@ -6,12 +6,14 @@ the C entry point, and a non-zero status raises NF4Error.  Every step of the
 computation runs in the library's HIP kernels; nothing here computes.
 
 Tensor conventions (all on the same CUDA/HIP device, contiguous):
-  packed         uint8  [N*K/2]  (any shape with that many bytes)
+  packed         uint8  [N*K/2]  (any shape with that many bytes); [N*K] for
+                 the 8-bit blockwise formats
   absmax         float32 [nb] (plain) or uint8 [nb] (nested)
   nested_absmax  float32 [ng] or None
   nested_offset  float32 [1] or None
-  code           float32 [16]
+  code           float32 [16] (4-bit) or [256] (8-bit)
   nested_code    float32 [256] or None
+A weight's `bits` (4 or 8) selects the C entry points: nf4_* or nf4_*_8bit.
 """
 
 from __future__ import annotations
@@ -61,6 +63,7 @@ class NF4Weight:
     nested_code: Optional[torch.Tensor]
     N: int
     K: int
+    bits: int = 4        # 4: packed nibbles, 16-entry code; 8: one byte, 256-entry code
 
     @property
     def nested(self) -> bool:
@@ -75,7 +78,7 @@ class NF4Weight:
         (the form the grouped calls take)."""
         if self.N % E:
             raise ValueError(f"{self.N} rows do not split into {E} experts")
-        return NF4Weight(*self.tensors(), self.N // E, self.K)
+        return NF4Weight(*self.tensors(), self.N // E, self.K, self.bits)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.tensors()[:4] if t is not None)
@@ -83,9 +86,11 @@ class NF4Weight:
 
 def _check_w(w: NF4Weight, rows: int):
     dev = w.packed.device
+    if w.bits not in (4, 8):
+        raise ValueError(f"bits must be 4 or 8, got {w.bits}")
     nb = L.lib().nf4_absmax_count(rows, w.K)
-    _need(w.packed, "packed", torch.uint8, rows * w.K // 2)
-    _need(w.code, "code", torch.float32, 16, dev)
+    _need(w.packed, "packed", torch.uint8, rows * w.K // 2 if w.bits == 4 else rows * w.K)
+    _need(w.code, "code", torch.float32, 16 if w.bits == 4 else 256, dev)
     if w.nested:
         ng = L.lib().nf4_nested_count(rows, w.K)
         _need(w.absmax, "absmax", torch.uint8, nb, dev)
@@ -116,9 +121,25 @@ def _workspace(op: int, M: int, N: int, K: int, E: int, device, ws: Optional[tor
     return buf, need
 
 
+def _fn(name: str, bits: int):
+    return getattr(L.lib(), name if bits == 4 else name + "_8bit")
+
+
+def nf4_quantize_8bit(w: torch.Tensor, code: torch.Tensor, nested_code: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None) -> NF4Weight:
+    """Quantise w [N, K] to an 8-bit blockwise format: one byte per weight,
+    an index into the ascending 256-entry table `code` (int8 map, fp8 e4m3
+    codebook, ...), the same 64-element blocks and statistics as NF4."""
+    return nf4_quantize(w, code, nested_code, ws, bits=8)
+
+
 def nf4_quantize(w: torch.Tensor, code: torch.Tensor, nested_code: Optional[torch.Tensor] = None,
-                 ws: Optional[torch.Tensor] = None) -> NF4Weight:
-    """Quantise w [N, K] (fp32 or bf16 device tensor) to NF4."""
+                 ws: Optional[torch.Tensor] = None, bits: int = 4) -> NF4Weight:
+    """Quantise w [N, K] (fp32 or bf16 device tensor) to NF4 (or, with
+    bits=8, to the 8-bit blockwise format of the 256-entry `code`)."""
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    _need(code, "code", torch.float32, 16 if bits == 4 else 256)
     if w.dim() != 2:
         raise ValueError("w must be [N, K]")
     _need(w, "w")
@@ -128,7 +149,7 @@ def nf4_quantize(w: torch.Tensor, code: torch.Tensor, nested_code: Optional[torc
     dev = w.device
     lib = L.lib()
     nb = lib.nf4_absmax_count(N, K)
-    packed = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    packed = torch.empty(N * K // 2 if bits == 4 else N * K, dtype=torch.uint8, device=dev)
     nested = nested_code is not None
     if nested:
         absmax = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -139,11 +160,11 @@ def nf4_quantize(w: torch.Tensor, code: torch.Tensor, nested_code: Optional[torc
         nabs = noff = None
     wsb, wsn = _workspace(L.NF4_OP_QUANTIZE, 0, N, K, 1, dev, ws) if nested else (None, 0)
     dt = L.NF4_DTYPE_BF16 if w.dtype == torch.bfloat16 else L.NF4_DTYPE_F32
-    st = lib.nf4_quantize(w.data_ptr(), dt, N, K, code.data_ptr(), _ptr(nested_code),
-                          packed.data_ptr(), absmax.data_ptr(), _ptr(nabs), _ptr(noff),
-                          _ptr(wsb), wsn, _stream())
-    L.check("nf4_quantize", st)
-    return NF4Weight(packed, absmax, nabs, noff, code, nested_code if nested else None, N, K)
+    st = _fn("nf4_quantize", bits)(w.data_ptr(), dt, N, K, code.data_ptr(), _ptr(nested_code),
+                                   packed.data_ptr(), absmax.data_ptr(), _ptr(nabs), _ptr(noff),
+                                   _ptr(wsb), wsn, _stream())
+    L.check("nf4_quantize" if bits == 4 else "nf4_quantize_8bit", st)
+    return NF4Weight(packed, absmax, nabs, noff, code, nested_code if nested else None, N, K, bits)
 
 
 def nf4_dequantize(w: NF4Weight, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None):
@@ -153,7 +174,7 @@ def nf4_dequantize(w: NF4Weight, out_dtype=torch.bfloat16, out: Optional[torch.T
         out = torch.empty((w.N, w.K), dtype=out_dtype, device=w.packed.device)
     _need(out, "out", out_dtype, w.N * w.K)
     dt = L.NF4_DTYPE_BF16 if out_dtype == torch.bfloat16 else L.NF4_DTYPE_F32
-    st = L.lib().nf4_dequantize(*_wargs(w), dt, out.data_ptr(), _stream())
+    st = _fn("nf4_dequantize", w.bits)(*_wargs(w), dt, out.data_ptr(), _stream())
     L.check("nf4_dequantize", st)
     return out
 
@@ -169,9 +190,10 @@ def nf4_matmul_fwd(x: torch.Tensor, w: NF4Weight, out: Optional[torch.Tensor] = 
     if out is None:
         out = torch.empty((M, w.N), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, M * w.N)
-    wsb, wsn = _workspace(L.NF4_OP_MATMUL_FWD, M, w.N, w.K, 1, x.device, ws)
-    st = L.lib().nf4_matmul_fwd(x.data_ptr(), M, *_wargs(w), out.data_ptr(), _ptr(wsb), wsn,
-                                _stream())
+    op = L.NF4_OP_MATMUL_FWD if w.bits == 4 else L.NF4_OP_MATMUL_FWD_8BIT
+    wsb, wsn = _workspace(op, M, w.N, w.K, 1, x.device, ws)
+    st = _fn("nf4_matmul_fwd", w.bits)(x.data_ptr(), M, *_wargs(w), out.data_ptr(), _ptr(wsb), wsn,
+                                       _stream())
     L.check("nf4_matmul_fwd", st)
     return out
 
@@ -187,9 +209,10 @@ def nf4_matmul_bwd_input(grad_y: torch.Tensor, w: NF4Weight, out: Optional[torch
     if out is None:
         out = torch.empty((M, w.K), dtype=torch.bfloat16, device=grad_y.device)
     _need(out, "out", torch.bfloat16, M * w.K)
-    wsb, wsn = _workspace(L.NF4_OP_MATMUL_BWD_INPUT, M, w.N, w.K, 1, grad_y.device, ws)
-    st = L.lib().nf4_matmul_bwd_input(grad_y.data_ptr(), M, *_wargs(w), out.data_ptr(),
-                                      _ptr(wsb), wsn, _stream())
+    op = L.NF4_OP_MATMUL_BWD_INPUT if w.bits == 4 else L.NF4_OP_MATMUL_BWD_INPUT_8BIT
+    wsb, wsn = _workspace(op, M, w.N, w.K, 1, grad_y.device, ws)
+    st = _fn("nf4_matmul_bwd_input", w.bits)(grad_y.data_ptr(), M, *_wargs(w), out.data_ptr(),
+                                             _ptr(wsb), wsn, _stream())
     L.check("nf4_matmul_bwd_input", st)
     return out
 
@@ -206,8 +229,8 @@ def nf4_grouped_matmul_fwd(x: torch.Tensor, offsets: torch.Tensor, w: NF4Weight,
     if out is None:
         out = torch.empty((T, w.N), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, T * w.N)
-    st = L.lib().nf4_grouped_matmul_fwd(x.data_ptr(), offsets.data_ptr(), E, T, *_wargs(w),
-                                        out.data_ptr(), None, 0, _stream())
+    st = _fn("nf4_grouped_matmul_fwd", w.bits)(x.data_ptr(), offsets.data_ptr(), E, T, *_wargs(w),
+                                               out.data_ptr(), None, 0, _stream())
     L.check("nf4_grouped_matmul_fwd", st)
     return out
 
@@ -224,8 +247,8 @@ def nf4_grouped_matmul_bwd_input(grad_y: torch.Tensor, offsets: torch.Tensor, w:
     if out is None:
         out = torch.empty((T, w.K), dtype=torch.bfloat16, device=grad_y.device)
     _need(out, "out", torch.bfloat16, T * w.K)
-    st = L.lib().nf4_grouped_matmul_bwd_input(grad_y.data_ptr(), offsets.data_ptr(), E, T,
-                                              *_wargs(w), out.data_ptr(), None, 0, _stream())
+    st = _fn("nf4_grouped_matmul_bwd_input", w.bits)(grad_y.data_ptr(), offsets.data_ptr(), E, T,
+                                                     *_wargs(w), out.data_ptr(), None, 0, _stream())
     L.check("nf4_grouped_matmul_bwd_input", st)
     return out
 

@@ -31,13 +31,13 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Checks shared by every call that takes the W-args.
 int check_w(const uint8_t* packed, const void* absmax, const float* nested_absmax,
             const float* nested_offset, const float* code16, const float* ncode, int64_t N,
-            int64_t K) {
+            int64_t K, int bits = 4) {
   if (N < 0 || K < 0) return NF4_ERR_SHAPE;
   if (N > 0 && K > INT64_MAX / N) return NF4_ERR_SHAPE;
   // a weight with no elements has no packed bytes or scales to point at
   if (!code16 || ((!packed || !absmax) && N * K != 0)) return NF4_ERR_NULL;
   if (nested_absmax && (!nested_offset || !ncode)) return NF4_ERR_NULL;
-  if ((N * K) % 2) return NF4_ERR_SHAPE;
+  if (bits == 4 && (N * K) % 2) return NF4_ERR_SHAPE;
   if (!aligned16(packed)) return NF4_ERR_ALIGN;
   return NF4_OK;
 }
@@ -101,9 +101,10 @@ int scratch_for_current_device(void** out) {
 int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed,
                   const void* absmax, const float* nested_absmax, const float* nested_offset,
                   const float* code16, const float* ncode, int64_t N, int64_t K, void* C,
-                  void* ws, size_t ws_bytes, void* stream, bool fixed_scratch = false) {
+                  void* ws, size_t ws_bytes, void* stream, bool fixed_scratch = false,
+                  int bits = 4) {
   const bool bwd = kind == GemmKind::kBwdInput;
-  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K);
+  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K, bits);
   if (st) return st;
   // an operand with no elements (empty batch, empty contraction, no output
   // columns) is never read or written and may be NULL, as torch gives for
@@ -120,7 +121,8 @@ int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed
     }
     return NF4_OK;
   }
-  const GemmPlan plan = plan_gemm(kind, M, N, K, device_cu_count());
+  const GemmPlan plan = bits == 8 ? plan_gemm8(kind, M, N, K, device_cu_count())
+                                  : plan_gemm(kind, M, N, K, device_cu_count());
   if (fixed_scratch) {
     if (plan.ws_bytes > ws_bytes) return NF4_ERR_SCRATCH;
     // set-up on the first call that reaches a launch on this device
@@ -129,7 +131,9 @@ int matmul_common(GemmKind kind, const void* A, int64_t M, const uint8_t* packed
   }
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return NF4_ERR_WORKSPACE;
   if (plan.ws_bytes > 0 && !aligned16(ws)) return NF4_ERR_ALIGN;
-  const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
+  WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
+  w.bits = bits;
+  if (bits == 8) return to_status(launch_gemm8(kind, plan, A, M, w, C, ws, static_cast<hipStream_t>(stream)));
   return to_status(launch_gemm(kind, plan, A, M, w, C, ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -137,14 +141,14 @@ int grouped_common(GemmKind kind, const void* A, const int32_t* offsets, int32_t
                    int64_t total_M, const uint8_t* packed, const void* absmax,
                    const float* nested_absmax, const float* nested_offset, const float* code16,
                    const float* ncode, int64_t N, int64_t K, void* C, void* ws, size_t ws_bytes,
-                   void* stream) {
+                   void* stream, int bits = 4) {
   (void)ws;
   (void)ws_bytes;
   const bool bwd = kind == GemmKind::kBwdInput;
   if (E < 1) return NF4_ERR_SHAPE;
   if (N < 0 || K < 0 || (N > 0 && E > INT64_MAX / N)) return NF4_ERR_SHAPE;
   int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, ncode,
-                   static_cast<int64_t>(E) * N, K);
+                   static_cast<int64_t>(E) * N, K, bits);
   if (st) return st;
   if (!offsets) return NF4_ERR_NULL;
   if (!A && total_M != 0 && (bwd ? N : K) != 0) return NF4_ERR_NULL;
@@ -158,10 +162,56 @@ int grouped_common(GemmKind kind, const void* A, const int32_t* offsets, int32_t
     }
     return NF4_OK;
   }
+  WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
+  w.bits = bits;
+  if (bits == 8)
+    return to_status(launch_grouped8(kind, A, offsets, E, total_M, w, C, static_cast<hipStream_t>(stream)));
   const GemmPlan plan = plan_grouped(kind, total_M, N, K, E);
-  const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, ncode, N, K};
   return to_status(launch_grouped(kind, plan, A, offsets, E, total_M, w, C,
                                   static_cast<hipStream_t>(stream)));
+}
+
+int quantize_common(const void* w, int w_dtype, int64_t N, int64_t K, const float* code16,
+                    const float* nested_code256, uint8_t* packed, void* absmax,
+                    float* nested_absmax, float* nested_offset, void* ws, size_t ws_bytes,
+                    void* stream, int bits) {
+  if (w_dtype != NF4_DTYPE_F32 && w_dtype != NF4_DTYPE_BF16) return NF4_ERR_DTYPE;
+  if (!w || !code16 || !packed || !absmax) return NF4_ERR_NULL;
+  const bool nested = nested_code256 != nullptr;
+  if (nested && (!nested_absmax || !nested_offset)) return NF4_ERR_NULL;
+  if (N < 0 || K < 0) return NF4_ERR_SHAPE;
+  if (N > 0 && K > INT64_MAX / N) return NF4_ERR_SHAPE;
+  const int64_t n = N * K;
+  if (bits == 4 && n % 2) return NF4_ERR_SHAPE;
+  if (n == 0) return NF4_OK;
+  if (!aligned16(packed) || !aligned16(w)) return NF4_ERR_ALIGN;
+  const size_t need = quantize_ws_bytes(n, nested);
+  if (need > 0 && (!ws || ws_bytes < need)) return NF4_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(ws)) return NF4_ERR_ALIGN;
+  const hipError_t e = launch_quantize(w, w_dtype == NF4_DTYPE_BF16, n, code16, nested_code256,
+                                       packed, absmax, nested_absmax, nested_offset, ws,
+                                       static_cast<hipStream_t>(stream), bits);
+  if (e == hipSuccess) count_path(NF4_PATH_QUANTIZE);
+  return e == hipSuccess ? NF4_OK : NF4_ERR_HIP;
+}
+
+int dequantize_common(const uint8_t* packed, const void* absmax, const float* nested_absmax,
+                      const float* nested_offset, const float* code16,
+                      const float* nested_code256, int64_t N, int64_t K, int out_dtype, void* out,
+                      void* stream, int bits) {
+  if (out_dtype != NF4_DTYPE_F32 && out_dtype != NF4_DTYPE_BF16) return NF4_ERR_DTYPE;
+  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N, K, bits);
+  if (st) return st;
+  if (!out) return NF4_ERR_NULL;
+  if (!aligned16(out)) return NF4_ERR_ALIGN;
+  const int64_t n = N * K;
+  if (n == 0) return NF4_OK;
+  WArgs w{packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N, K};
+  w.bits = bits;
+  const hipError_t e = launch_dequantize(w, n, out_dtype == NF4_DTYPE_BF16, out,
+                                         static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) count_path(NF4_PATH_DEQUANTIZE);
+  return e == hipSuccess ? NF4_OK : NF4_ERR_HIP;
 }
 
 }  // namespace
@@ -174,41 +224,69 @@ extern "C" {
 int nf4_quantize(const void* w, int w_dtype, int64_t N, int64_t K, const float* code16,
                  const float* nested_code256, uint8_t* packed, void* absmax, float* nested_absmax,
                  float* nested_offset, void* ws, size_t ws_bytes, void* stream) {
-  if (w_dtype != NF4_DTYPE_F32 && w_dtype != NF4_DTYPE_BF16) return NF4_ERR_DTYPE;
-  if (!w || !code16 || !packed || !absmax) return NF4_ERR_NULL;
-  const bool nested = nested_code256 != nullptr;
-  if (nested && (!nested_absmax || !nested_offset)) return NF4_ERR_NULL;
-  if (N < 0 || K < 0) return NF4_ERR_SHAPE;
-  if (N > 0 && K > INT64_MAX / N) return NF4_ERR_SHAPE;
-  const int64_t n = N * K;
-  if (n % 2) return NF4_ERR_SHAPE;
-  if (n == 0) return NF4_OK;
-  if (!aligned16(packed) || !aligned16(w)) return NF4_ERR_ALIGN;
-  const size_t need = quantize_ws_bytes(n, nested);
-  if (need > 0 && (!ws || ws_bytes < need)) return NF4_ERR_WORKSPACE;
-  if (need > 0 && !aligned16(ws)) return NF4_ERR_ALIGN;
-  const hipError_t e = launch_quantize(w, w_dtype == NF4_DTYPE_BF16, n, code16, nested_code256,
-                                       packed, absmax, nested_absmax, nested_offset, ws,
-                                       static_cast<hipStream_t>(stream));
-  if (e == hipSuccess) count_path(NF4_PATH_QUANTIZE);
-  return e == hipSuccess ? NF4_OK : NF4_ERR_HIP;
+  return quantize_common(w, w_dtype, N, K, code16, nested_code256, packed, absmax, nested_absmax,
+                         nested_offset, ws, ws_bytes, stream, 4);
+}
+
+int nf4_quantize_8bit(const void* w, int w_dtype, int64_t N, int64_t K, const float* code256,
+                      const float* nested_code256, uint8_t* packed, void* absmax,
+                      float* nested_absmax, float* nested_offset, void* ws, size_t ws_bytes,
+                      void* stream) {
+  return quantize_common(w, w_dtype, N, K, code256, nested_code256, packed, absmax, nested_absmax,
+                         nested_offset, ws, ws_bytes, stream, 8);
 }
 
 int nf4_dequantize(const uint8_t* packed, const void* absmax, const float* nested_absmax,
                    const float* nested_offset, const float* code16, const float* nested_code256,
                    int64_t N, int64_t K, int out_dtype, void* out, void* stream) {
-  if (out_dtype != NF4_DTYPE_F32 && out_dtype != NF4_DTYPE_BF16) return NF4_ERR_DTYPE;
-  int st = check_w(packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N, K);
-  if (st) return st;
-  if (!out) return NF4_ERR_NULL;
-  if (!aligned16(out)) return NF4_ERR_ALIGN;
-  const int64_t n = N * K;
-  if (n == 0) return NF4_OK;
-  const WArgs w{packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N, K};
-  const hipError_t e = launch_dequantize(w, n, out_dtype == NF4_DTYPE_BF16, out,
-                                         static_cast<hipStream_t>(stream));
-  if (e == hipSuccess) count_path(NF4_PATH_DEQUANTIZE);
-  return e == hipSuccess ? NF4_OK : NF4_ERR_HIP;
+  return dequantize_common(packed, absmax, nested_absmax, nested_offset, code16, nested_code256, N,
+                           K, out_dtype, out, stream, 4);
+}
+
+int nf4_dequantize_8bit(const uint8_t* packed, const void* absmax, const float* nested_absmax,
+                        const float* nested_offset, const float* code256,
+                        const float* nested_code256, int64_t N, int64_t K, int out_dtype,
+                        void* out, void* stream) {
+  return dequantize_common(packed, absmax, nested_absmax, nested_offset, code256, nested_code256, N,
+                           K, out_dtype, out, stream, 8);
+}
+
+int nf4_matmul_fwd_8bit(const void* x, int64_t M, const uint8_t* packed, const void* absmax,
+                        const float* nested_absmax, const float* nested_offset,
+                        const float* code256, const float* nested_code256, int64_t N, int64_t K,
+                        void* y, void* ws, size_t ws_bytes, void* stream) {
+  return matmul_common(GemmKind::kFwd, x, M, packed, absmax, nested_absmax, nested_offset, code256,
+                       nested_code256, N, K, y, ws, ws_bytes, stream, false, 8);
+}
+
+int nf4_matmul_bwd_input_8bit(const void* grad_y, int64_t M, const uint8_t* packed,
+                              const void* absmax, const float* nested_absmax,
+                              const float* nested_offset, const float* code256,
+                              const float* nested_code256, int64_t N, int64_t K, void* grad_x,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return matmul_common(GemmKind::kBwdInput, grad_y, M, packed, absmax, nested_absmax,
+                       nested_offset, code256, nested_code256, N, K, grad_x, ws, ws_bytes, stream,
+                       false, 8);
+}
+
+int nf4_grouped_matmul_fwd_8bit(const void* x, const int32_t* offsets, int32_t E, int64_t total_M,
+                                const uint8_t* packed, const void* absmax,
+                                const float* nested_absmax, const float* nested_offset,
+                                const float* code256, const float* nested_code256, int64_t N,
+                                int64_t K, void* y, void* ws, size_t ws_bytes, void* stream) {
+  return grouped_common(GemmKind::kFwd, x, offsets, E, total_M, packed, absmax, nested_absmax,
+                        nested_offset, code256, nested_code256, N, K, y, ws, ws_bytes, stream, 8);
+}
+
+int nf4_grouped_matmul_bwd_input_8bit(const void* grad_y, const int32_t* offsets, int32_t E,
+                                      int64_t total_M, const uint8_t* packed, const void* absmax,
+                                      const float* nested_absmax, const float* nested_offset,
+                                      const float* code256, const float* nested_code256,
+                                      int64_t N, int64_t K, void* grad_x, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  return grouped_common(GemmKind::kBwdInput, grad_y, offsets, E, total_M, packed, absmax,
+                        nested_absmax, nested_offset, code256, nested_code256, N, K, grad_x, ws,
+                        ws_bytes, stream, 8);
 }
 
 int nf4_matmul_fwd(const void* x, int64_t M, const uint8_t* packed, const void* absmax,
@@ -274,6 +352,12 @@ size_t nf4_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int32_t E) {
     case NF4_OP_GROUPED_BWD_INPUT:
       if (E < 1) return SIZE_MAX;
       return 0;
+    case NF4_OP_MATMUL_FWD_8BIT:
+    case NF4_OP_MATMUL_BWD_INPUT_8BIT: {
+      if (M == 0 || N == 0 || K == 0) return 0;
+      const GemmKind kind = op == NF4_OP_MATMUL_FWD_8BIT ? GemmKind::kFwd : GemmKind::kBwdInput;
+      return plan_gemm8(kind, M, N, K, device_cu_count()).ws_bytes;
+    }
     default:
       return SIZE_MAX;
   }

@@ -219,6 +219,90 @@ __global__ __launch_bounds__(kThreads) void k_dequant_f32(WArgs w, int64_t n,
   }
 }
 
+// ---- 8-bit blockwise variants (one index per byte, 256-entry table) --------------
+// The bitsandbytes fork PR "Experts trainability ... ExpertsNbit", "Commit 1"
+// table lists 8-bit blockwise formats (int8 map, fp8 e4m3 codebook) with the
+// same 64-element blocks; the 256-entry table is an argument, the index is
+// the number of table midpoints strictly below t (binary search in LDS).
+
+// One thread per 8 consecutive elements, 8 threads per 64-block.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_quant_blocks8(const T* __restrict__ w, int64_t n,
+                                                            const float* __restrict__ code,
+                                                            uint8_t* __restrict__ packed,
+                                                            float* __restrict__ absmax_out) {
+  __shared__ float mid[256];
+  if (threadIdx.x < 255) mid[threadIdx.x] = __fmul_rn(__fadd_rn(code[threadIdx.x], code[threadIdx.x + 1]), 0.5f);
+  __syncthreads();
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;  // 8-group
+  const int64_t e0 = g * 8;
+  float v[8];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = (e0 + i < n) ? load_w(w, e0 + i) : 0.f;
+    m = fmaxf(m, fabsf(v[i]));
+  }
+  m = fmaxf(m, __shfl_xor(m, 1, 8));
+  m = fmaxf(m, __shfl_xor(m, 2, 8));
+  m = fmaxf(m, __shfl_xor(m, 4, 8));
+  if (e0 >= n) return;
+  uint32_t word[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = (m == 0.f) ? 0.f : v[i] / m;   // correctly rounded division
+    int lo = 0, hi = 255;                           // first j with !(t > mid[j])
+    while (lo < hi) {
+      const int md = (lo + hi) >> 1;
+      if (t > mid[md]) lo = md + 1; else hi = md;
+    }
+    word[i >> 2] |= static_cast<uint32_t>(lo) << (8 * (i & 3));
+  }
+  if (e0 + 8 <= n) {
+    reinterpret_cast<u32x2_t*>(packed)[g] = u32x2_t{word[0], word[1]};
+  } else {
+    for (int64_t i = e0; i < n; ++i) packed[i] = static_cast<uint8_t>(word[(i - e0) >> 2] >> (8 * ((i - e0) & 3)));
+  }
+  if ((g & 7) == 0) absmax_out[g >> 3] = m;
+}
+
+// Dequantisation: one thread per 8 elements, the table in LDS.
+template <bool NESTED, bool BF16>
+__global__ __launch_bounds__(kThreads) void k_dequant8(WArgs w, int64_t n, void* __restrict__ out) {
+  __shared__ float sncode[256];
+  __shared__ float scode[256];
+  scode[threadIdx.x] = w.code[threadIdx.x];
+  float off = 0.f;
+  if constexpr (NESTED) {
+    sncode[threadIdx.x] = w.ncode[threadIdx.x];
+    off = w.nested_offset[0];
+  }
+  __syncthreads();
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t e0 = g * 8;
+  if (e0 >= n) return;
+  const float a = block_scale<NESTED>(w.absmax, w.nested_absmax, off, sncode, e0 / kBlock);
+  float v[8];
+  if (e0 + 8 <= n) {
+    const u32x2_t p = reinterpret_cast<const u32x2_t*>(w.packed)[g];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __fmul_rn(scode[(p[i >> 2] >> (8 * (i & 3))) & 0xFFu], a);
+    if constexpr (BF16) {
+      reinterpret_cast<u32x4_t*>(out)[g] = u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                   pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else {
+      reinterpret_cast<f32x4_t*>(out)[2 * g] = f32x4_t{v[0], v[1], v[2], v[3]};
+      reinterpret_cast<f32x4_t*>(out)[2 * g + 1] = f32x4_t{v[4], v[5], v[6], v[7]};
+    }
+  } else {
+    for (int64_t i = e0; i < n; ++i) {
+      const float x = __fmul_rn(scode[w.packed[i]], a);
+      if constexpr (BF16) static_cast<uint16_t*>(out)[i] = to_bf16(x);
+      else static_cast<float*>(out)[i] = x;
+    }
+  }
+}
+
 inline unsigned grid_for(int64_t items) {
   return static_cast<unsigned>((items + kThreads - 1) / kThreads);
 }
@@ -237,13 +321,21 @@ size_t quantize_ws_bytes(int64_t n_elems, bool nested) {
 hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, const float* code,
                            const float* ncode, uint8_t* packed, void* absmax,
                            float* nested_absmax, float* nested_offset, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, int bits) {
   const bool nested = ncode != nullptr;
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kNestedBlock - 1) / kNestedBlock;
   float* am32 = nested ? static_cast<float*>(ws) : static_cast<float*>(absmax);
   const int64_t groups8 = (n + 7) / 8;
-  if (w_is_bf16) {
+  if (bits == 8) {
+    if (w_is_bf16) {
+      k_quant_blocks8<uint16_t><<<grid_for(groups8), kThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(w), n, code, packed, am32);
+    } else {
+      k_quant_blocks8<float><<<grid_for(groups8), kThreads, 0, stream>>>(
+          static_cast<const float*>(w), n, code, packed, am32);
+    }
+  } else if (w_is_bf16) {
     k_quant_blocks<uint16_t><<<grid_for(groups8), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(w), n, code, packed, am32);
   } else {
@@ -264,6 +356,16 @@ hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, const float
 hipError_t launch_dequantize(const WArgs& w, int64_t n, bool out_bf16, void* out,
                              hipStream_t stream) {
   const unsigned grid = grid_for((n + 7) / 8);
+  if (w.bits == 8) {
+    if (w.nested()) {
+      if (out_bf16) k_dequant8<true, true><<<grid, kThreads, 0, stream>>>(w, n, out);
+      else k_dequant8<true, false><<<grid, kThreads, 0, stream>>>(w, n, out);
+    } else {
+      if (out_bf16) k_dequant8<false, true><<<grid, kThreads, 0, stream>>>(w, n, out);
+      else k_dequant8<false, false><<<grid, kThreads, 0, stream>>>(w, n, out);
+    }
+    return hipGetLastError();
+  }
   if (out_bf16) {
     if (w.nested())
       k_dequant_bf16<true><<<grid, kThreads, 0, stream>>>(w, n, static_cast<uint16_t*>(out));

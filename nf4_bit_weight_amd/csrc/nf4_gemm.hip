@@ -1446,6 +1446,226 @@ __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restr
   }
 }
 
+// ---------------------------------------------------------------------------------
+// 8-bit blockwise fused GEMM: forward and input gradient, plain and grouped.
+//
+// The weight is one index per byte into a 256-entry table (bitsandbytes fork
+// PR "Experts trainability ... ExpertsNbit", "Commit 1": int8 and fp8 e4m3
+// blockwise beside nf4 / fp4), w_hat = bf16(fp32(code[q] * absmax_hat)) with
+// the same 64-element blocks and (nested) scales.  A 256-entry table per
+// (row, block) does not fit the register byte tables of the 4-bit kernels, so
+// the table itself (256 fp32) sits in LDS and each weight costs one LDS
+// lookup, one fp32 multiply and half a packed bf16 conversion.
+//
+// Tile BM x 128 (BM = 128, or 32 for M <= 32 where it streams the weights
+// once with the contraction split across workgroups), BK = 64, four waves
+// (2 x 2 of 64 x 64, or 1 x 4 of 32 x 32), v_mfma_f32_32x32x16_bf16.  Every
+// step the threads load the next step's activation vectors and 32 weight
+// bytes each into registers, the waves multiply the current LDS buffers, and
+// the threads then store the activations and expand their 32 weights into the
+// other buffer; one barrier per step.  Both LDS tiles are stored
+// [output-or-activation row][contraction] with rows of 64 + 8 elements, so
+// every MFMA fragment is one 16-byte read: the forward expands 32 contiguous
+// contraction elements of one W row, the input gradient 32 output columns
+// of one W row (stored one element per column row).
+template <int BM>
+struct G8 {
+  static constexpr int BN = 128, BK = 64, kPitch = BK + 8;
+  static constexpr int WAVES_M = BM == 128 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int MI = WM / 32, NI = WN / 32;
+  static constexpr int kA = BM * kPitch, kB = BN * kPitch;     // elements per buffer
+  static constexpr int kAVec = BM * BK / 8 / 256;              // 16-byte activation vectors per thread
+  static constexpr int kLds = 2 * (kA + kB) * 2;
+};
+
+template <int BM, bool TRANS, bool NESTED, bool GROUPED>
+__global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
+  using G = G8<BM>;
+  constexpr int BN = G::BN, BK = G::BK, P = G::kPitch;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  __shared__ float scode[256];
+  __shared__ float sncode[256];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t N = p.w.N, K = p.w.K;
+  const int64_t Nc = TRANS ? K : N;
+  const int64_t Kc = TRANS ? N : K;
+  const int ktiles = static_cast<int>((Kc + BK - 1) / BK);
+
+  const int tt = xcd_tile(blockIdx.x, gridDim.x);
+  const int mt = tt % p.m_tiles;
+  const int cz = tt / p.m_tiles;
+  const int z = cz % p.splits;
+  const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
+  int64_t row0, row_end, wrow_base;
+  if (!row_tile<BM, GROUPED>(p, mt, N, row0, row_end, wrow_base)) return;
+  const int kb = static_cast<int>(static_cast<int64_t>(z) * ktiles / p.splits);
+  const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
+  const int n = ke - kb;
+
+  scode[tid] = p.w.code[tid];
+  if constexpr (NESTED) sncode[tid] = p.w.ncode[tid];
+  const float off = NESTED ? p.w.nested_offset[0] : 0.f;
+
+  auto a_buf = [&](int b) { return lds + b * G::kA; };
+  auto b_buf = [&](int b) { return lds + 2 * G::kA + b * G::kB; };
+
+  // ---- this thread's loads ---------------------------------------------------------
+  // activation vector j: row (tid + 256 j) / 8, 16-byte unit (tid + 256 j) % 8;
+  // rows past the end repeat the last row, columns past Kc repeat the last
+  // vector (they meet zero weights or are never stored)
+  const uint16_t* a_row[G::kAVec];
+  int a_c8[G::kAVec], a_dst[G::kAVec];
+#pragma unroll
+  for (int j = 0; j < G::kAVec; ++j) {
+    const int u = tid + 256 * j;
+    const int r = u >> 3;
+    int64_t row = row0 + r;
+    row = row < row_end ? row : row_end - 1;
+    a_row[j] = p.A + row * Kc;
+    a_c8[j] = 8 * (u & 7);
+    a_dst[j] = r * P + a_c8[j];
+  }
+  // weights: forward, W row col0 + tid/2, contraction 32 (tid%2) .. +31 of the
+  // step; input gradient, W row (step row) tid/4, output columns col0 +
+  // 32 (tid%4) .. +31.  Invalid pieces read byte 0 of the tensor and get a
+  // zero scale.
+  const int wl = TRANS ? (tid >> 2) : (tid >> 1);
+  const int wq = TRANS ? (tid & 3) : (tid & 1);
+  const int64_t kblocks = K / BK;
+  struct Regs {
+    u32x4_t a[G::kAVec];
+    u32x4_t w0, w1;
+    uint32_t sc, s2;
+    bool ok;
+  };
+  auto load = [&](int i, Regs& r) __attribute__((always_inline)) {
+    const int kt = kb + i;
+    const int64_t c = static_cast<int64_t>(kt) * BK;
+#pragma unroll
+    for (int j = 0; j < G::kAVec; ++j) {
+      const int64_t cc = c + a_c8[j];
+      r.a[j] = *reinterpret_cast<const u32x4_t*>(a_row[j] + (cc + 8 <= Kc ? cc : Kc - 8));
+    }
+    int64_t wrow, wcol;
+    if constexpr (TRANS) {
+      wrow = static_cast<int64_t>(kt) * BK + wl;
+      wcol = col0 + 32 * wq;
+      r.ok = wrow < N && wcol < K;
+    } else {
+      wrow = col0 + wl;
+      wcol = static_cast<int64_t>(kt) * BK + 32 * wq;
+      r.ok = wrow < N;
+    }
+    const int64_t grow = wrow_base + (r.ok ? wrow : 0);
+    const int64_t e0 = r.ok ? grow * K + wcol : 0;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + e0);
+    r.w0 = src[0];
+    r.w1 = src[1];
+    const int64_t b = r.ok ? grow * kblocks + (wcol >> 6) : 0;
+    if constexpr (NESTED) {
+      r.sc = static_cast<const uint8_t*>(p.w.absmax)[b];
+      r.s2 = __float_as_uint(p.w.nested_absmax[b >> 8]);
+    } else {
+      r.sc = __float_as_uint(static_cast<const float*>(p.w.absmax)[b]);
+      r.s2 = 0;
+    }
+  };
+  auto store = [&](int buf, const Regs& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < G::kAVec; ++j) *reinterpret_cast<u32x4_t*>(a_buf(buf) + a_dst[j]) = r.a[j];
+    float a;
+    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[r.sc & 0xFF], __uint_as_float(r.s2)), off);
+    else a = __uint_as_float(r.sc);
+    a = r.ok ? a : 0.f;
+    uint32_t o[16];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t wd = d < 4 ? r.w0[d] : r.w1[d - 4];
+      const float v0 = __fmul_rn(scode[wd & 0xFFu], a), v1 = __fmul_rn(scode[(wd >> 8) & 0xFFu], a);
+      const float v2 = __fmul_rn(scode[(wd >> 16) & 0xFFu], a), v3 = __fmul_rn(scode[wd >> 24], a);
+      o[2 * d] = pack_bf16x2(v0, v1);
+      o[2 * d + 1] = pack_bf16x2(v2, v3);
+    }
+    uint16_t* bb = b_buf(buf);
+    if constexpr (TRANS) {
+      // element i of the piece is W_hat[row wl, column 32 wq + i]: output row 32 wq + i
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        bb[(32 * wq + i) * P + wl] = static_cast<uint16_t>(o[i >> 1] >> (16 * (i & 1)));
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        *reinterpret_cast<u32x4_t*>(bb + wl * P + 32 * wq + 8 * d) =
+            u32x4_t{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]};
+    }
+  };
+
+  // ---- MFMA part ------------------------------------------------------------------
+  const int wm = wave / G::WAVES_N, wn = wave % G::WAVES_N;
+  const int r32 = lane & 31, h = lane >> 5;
+  f32x16_t acc[G::MI][G::NI];
+#pragma unroll
+  for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const uint16_t* ab = a_buf(buf) + (wm * G::WM + r32) * P + 8 * h;
+    const uint16_t* bb = b_buf(buf) + (wn * G::WN + r32) * P + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t fa[G::MI], fb[G::NI];
+#pragma unroll
+      for (int i = 0; i < G::MI; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(ab + 32 * i * P + 16 * kk);
+#pragma unroll
+      for (int j = 0; j < G::NI; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(bb + 32 * j * P + 16 * kk);
+#pragma unroll
+      for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < G::NI; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  __syncthreads();                                     // tables in LDS
+  if (n > 0) {
+    Regs r;
+    load(0, r);
+    store(0, r);
+    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+      if (i + 1 < n) load(i + 1, r);
+      compute(i & 1);
+      if (i + 1 < n) store((i + 1) & 1, r);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------------
+#pragma unroll
+  for (int i = 0; i < G::MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < G::NI; ++j) {
+      const int64_t col = col0 + wn * G::WN + 32 * j + r32;
+      if (col >= Nc) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + wm * G::WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row >= row_end) continue;
+        if (p.splits == 1) {
+          p.C[row * Nc + col] = to_bf16(acc[i][j][v]);
+        } else {
+          p.partial[(static_cast<int64_t>(z) * p.M + row) * Nc + col] = acc[i][j][v];
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, bool TRANS, bool NESTED, bool GROUPED, int C>
 hipError_t launch_tiled(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
   using T = Tile<BM, BN, TRANS, C>;
@@ -1767,6 +1987,118 @@ hipError_t launch_grouped(GemmKind kind, const GemmPlan& plan, const void* A,
                        : dispatch_tile<false, true>(plan.bm, plan.bn, plan.consumers, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 7 : 6);
+  return hipSuccess;
+}
+
+}  // namespace nf4
+
+// ---- 8-bit blockwise matmuls ------------------------------------------------------
+namespace nf4 {
+namespace {
+
+template <int BM, bool TRANS, bool NESTED, bool GROUPED>
+hipError_t launch_g8_t(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
+  auto kern = k_gemm8<BM, TRANS, NESTED, GROUPED>;
+  static const bool attr_done = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, G8<BM>::kLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)attr_done;
+  GemmParams q = p;
+  q.m_tiles = static_cast<int32_t>(m_tiles);
+  const int64_t tiles = ((n_cols + G8<BM>::BN - 1) / G8<BM>::BN) * m_tiles * p.splits;
+  if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kern<<<dim3(static_cast<unsigned>(tiles)), 256, G8<BM>::kLds, stream>>>(q);
+  return hipGetLastError();
+}
+
+template <bool TRANS, bool GROUPED>
+hipError_t dispatch_g8(int bm, const GemmParams& p, int64_t m_tiles, int64_t n_cols,
+                       hipStream_t stream) {
+  const bool nested = p.w.nested();
+  if (bm == 32)
+    return nested ? launch_g8_t<32, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
+                  : launch_g8_t<32, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
+  return nested ? launch_g8_t<128, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
+                : launch_g8_t<128, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
+}
+
+}  // namespace
+
+// 128-row tiles, or 32 at M <= 32; the contraction is split (powers of two up
+// to 16) while the tiles alone leave compute units idle and every split keeps
+// at least two 64-deep steps.
+GemmPlan plan_gemm8(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
+  GemmPlan pl{};
+  const int64_t nc = (kind == GemmKind::kFwd) ? N : K;
+  const int64_t kc = (kind == GemmKind::kFwd) ? K : N;
+  pl.bm = M <= 32 ? 32 : 128;
+  pl.bn = 128;
+  pl.consumers = 0;
+  pl.small_m = false;
+  pl.kc = 0;
+  const int64_t tiles = (M + pl.bm - 1) / pl.bm * ((nc + 127) / 128);
+  const int64_t ktiles = (kc + 63) / 64;
+  int s = 1;
+  while (s < 16 && tiles * s < cus && ktiles / (2 * s) >= 2) s *= 2;
+  pl.splits = s;
+  pl.ws_bytes = s > 1 ? static_cast<size_t>(s) * static_cast<size_t>(M) * static_cast<size_t>(nc) * 4 : 0;
+  return pl;
+}
+
+hipError_t launch_gemm8(GemmKind kind, const GemmPlan& plan, const void* A, int64_t M,
+                        const WArgs& w, void* C, void* ws, hipStream_t stream) {
+  const bool trans = kind == GemmKind::kBwdInput;
+  const int64_t nc = trans ? w.K : w.N;
+  GemmParams p{};
+  p.A = static_cast<const uint16_t*>(A);
+  p.C = static_cast<uint16_t*>(C);
+  p.partial = static_cast<float*>(ws);
+  p.w = w;
+  p.offsets = nullptr;
+  p.M = M;
+  p.E = 1;
+  p.splits = plan.splits;
+  const int64_t m_tiles = (M + plan.bm - 1) / plan.bm;
+  hipError_t e = trans ? dispatch_g8<true, false>(plan.bm, p, m_tiles, nc, stream)
+                       : dispatch_g8<false, false>(plan.bm, p, m_tiles, nc, stream);
+  if (e != hipSuccess) return e;
+  count_path(trans ? 9 : 8);
+  if (plan.splits > 1) {
+    const int64_t n = M * nc;
+    const int64_t threads = (n + 3) / 4;
+    k_splitk_reduce<<<static_cast<unsigned>((threads + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+        static_cast<const float*>(ws), plan.splits, n, static_cast<uint16_t*>(C));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    count_path(5);
+  }
+  return hipSuccess;
+}
+
+// Grouped: 32-row tiles when experts hold 48 rows or fewer on average, else
+// 128; no split.
+hipError_t launch_grouped8(GemmKind kind, const void* A, const int32_t* offsets, int32_t E,
+                           int64_t total_M, const WArgs& w, void* C, hipStream_t stream) {
+  const bool trans = kind == GemmKind::kBwdInput;
+  const int64_t nc = trans ? w.K : w.N;
+  const int bm = total_M <= 48 * static_cast<int64_t>(E) ? 32 : 128;
+  GemmParams p{};
+  p.A = static_cast<const uint16_t*>(A);
+  p.C = static_cast<uint16_t*>(C);
+  p.partial = nullptr;
+  p.w = w;
+  p.offsets = offsets;
+  p.M = total_M;
+  p.E = E;
+  p.splits = 1;
+  const int64_t m_tiles = (total_M + bm - 1) / bm + E;
+  hipError_t e = trans ? dispatch_g8<true, true>(bm, p, m_tiles, nc, stream)
+                       : dispatch_g8<false, true>(bm, p, m_tiles, nc, stream);
+  if (e != hipSuccess) return e;
+  count_path(trans ? 9 : 8);
   return hipSuccess;
 }
 

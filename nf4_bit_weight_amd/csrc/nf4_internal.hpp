@@ -17,6 +17,8 @@ struct WArgs {
   const float* code;           // 16 fp32
   const float* ncode;          // 256 fp32 (nested only)
   int64_t N, K;
+  int32_t bits = 4;            // 4: NF4-style packed nibbles, 16-entry code;
+                               // 8: one index per byte, 256-entry code
   bool nested() const { return nested_absmax != nullptr; }
 };
 
@@ -25,7 +27,7 @@ size_t quantize_ws_bytes(int64_t n_elems, bool nested);
 hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n_elems, const float* code,
                            const float* ncode, uint8_t* packed, void* absmax,
                            float* nested_absmax, float* nested_offset, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, int bits = 4);
 hipError_t launch_dequantize(const WArgs& w, int64_t n_elems, bool out_bf16, void* out,
                              hipStream_t stream);
 
@@ -58,6 +60,14 @@ hipError_t launch_gemm(GemmKind kind, const GemmPlan& plan, const void* A, int64
 hipError_t launch_grouped(GemmKind kind, const GemmPlan& plan, const void* A,
                           const int32_t* offsets, int32_t E, int64_t total_M, const WArgs& w,
                           void* C, hipStream_t stream);
+
+// 8-bit blockwise matmuls (one index per byte, 256-entry table): their own
+// tiled kernel (nf4_gemm.hip), 128 or 32 activation rows per tile
+GemmPlan plan_gemm8(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus);
+hipError_t launch_gemm8(GemmKind kind, const GemmPlan& plan, const void* A, int64_t M,
+                        const WArgs& w, void* C, void* ws, hipStream_t stream);
+hipError_t launch_grouped8(GemmKind kind, const void* A, const int32_t* offsets, int32_t E,
+                           int64_t total_M, const WArgs& w, void* C, hipStream_t stream);
 
 // path counters (defined in nf4_abi.hip)
 void count_path(int path);

@@ -34,7 +34,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
         assert n in L.SIGNATURES, f"binding lacks {n}"
@@ -46,7 +46,8 @@ def test_header_macros_match_binding():
     for name in ("NF4_OK", "NF4_ERR_NULL", "NF4_ERR_SHAPE", "NF4_ERR_UNSUPPORTED",
                  "NF4_ERR_ALIGN", "NF4_ERR_WORKSPACE", "NF4_ERR_HIP", "NF4_ERR_DTYPE", "NF4_ERR_SCRATCH",
                  "NF4_DTYPE_F32", "NF4_DTYPE_BF16", "NF4_OP_QUANTIZE", "NF4_OP_MATMUL_FWD",
-                 "NF4_OP_MATMUL_BWD_INPUT", "NF4_OP_GROUPED_FWD", "NF4_OP_GROUPED_BWD_INPUT"):
+                 "NF4_OP_MATMUL_BWD_INPUT", "NF4_OP_GROUPED_FWD", "NF4_OP_GROUPED_BWD_INPUT",
+                 "NF4_OP_MATMUL_FWD_8BIT", "NF4_OP_MATMUL_BWD_INPUT_8BIT"):
         assert int(vals[name]) == getattr(L, name), name
     assert int(vals["NF4_PATH_COUNT"]) == len(L.PATHS)
 
@@ -179,3 +180,25 @@ def test_noalloc_validation(lib):
     text = open(HEADER).read()
     assert f"#define NF4_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
     assert L.NF4_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_8bit_validation(lib):
+    """The 8-bit entry points validate like the 4-bit ones; an odd element
+    count is allowed (one byte per weight) and the 8-bit workspace comes from
+    its own op codes."""
+    def f(x=FAKE, M=4, packed=FAKE, N=8, K=64, y=FAKE, ws=None, wsb=0):
+        return lib.nf4_matmul_fwd_8bit(x, M, packed, FAKE, None, None, FAKE, None, N, K, y, ws, wsb, None)
+    assert f(x=None) == L.NF4_ERR_NULL
+    assert f(packed=None) == L.NF4_ERR_NULL
+    assert f(K=96) == L.NF4_ERR_UNSUPPORTED
+    assert f(M=0) == L.NF4_OK
+    q = lib.nf4_quantize_8bit
+    assert q(None, 0, 3, 5, FAKE, None, FAKE, FAKE, None, None, None, 0, None) == L.NF4_ERR_NULL
+    assert q(FAKE, 9, 4, 64, FAKE, None, FAKE, FAKE, None, None, None, 0, None) == L.NF4_ERR_DTYPE
+    M, N, K = 8, 1024, 4096
+    need = lib.nf4_workspace_bytes(L.NF4_OP_MATMUL_FWD_8BIT, M, N, K, 1)
+    assert need > 0                                          # few tiles: contraction split
+    assert f(M=M, N=N, K=K) == L.NF4_ERR_WORKSPACE
+    assert lib.nf4_workspace_bytes(L.NF4_OP_MATMUL_BWD_INPUT_8BIT, 0, N, K, 1) == 0
+    d = lib.nf4_dequantize_8bit
+    assert d(FAKE, FAKE, None, None, FAKE, None, 4, 64, 7, FAKE, None) == L.NF4_ERR_DTYPE
