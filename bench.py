@@ -42,11 +42,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", default=None, metavar="DIR_PROJ",
-                    help="time one shape of the step (e.g. fwd_gate: the 32 layers' forward gate "
-                         "projections) and nothing else; used for profiling")
+    ap.add_argument("--only", default=None, metavar="[FAMILY:]DIR_PROJ",
+                    help="time one shape and nothing else, for profiling: fwd_gate (the 32 layers' "
+                         "forward gate projections of the step), qwen:bwd_down, olmoe:fwd_gate")
     ap.add_argument("--m", type=int, default=0,
-                    help="with --only: rows of x (default: the step's M = 512)")
+                    help="with --only: rows of x (default: the workload's M, 512 or 2048)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only: then run one plain device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -84,12 +84,75 @@ def timed(torch, stream, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def filler_copy(torch, dev, nbytes=1 << 30):
+    """A device copy of 1 GiB (~0.4 ms) enqueued before each timed sample: the
+    GPU works through it while the host enqueues the sample's calls, so the
+    sample measures GPU time even where one call launches slower from Python
+    than it runs, and every sample starts with the caches refilled by
+    unrelated data."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    return lambda: dst.copy_(src)
+
+
+def interleaved(torch, stream, arms, filler, rounds=21, reps=5, warmup=2):
+    """Median time per call of each arm.  Every round runs each arm once (reps
+    calls between two HIP events on the launch stream, after the filler), in
+    an order rotated from round to round, so slow drift of clocks or
+    temperature falls on all arms alike."""
+    names = list(arms)
+    for _ in range(warmup):
+        for n in names:
+            arms[n]()
+    pairs = {n: [] for n in names}
+    for r in range(rounds):
+        k = r % len(names)
+        for n in names[k:] + names[:k]:
+            filler()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                arms[n]()
+            b.record(stream)
+            pairs[n].append((a, b))
+    torch.cuda.synchronize()
+    out = {}
+    for n in names:
+        t = sorted(a.elapsed_time(b) * 1e3 / reps for a, b in pairs[n])
+        out[n] = {"median_us": round(t[len(t) // 2], 2), "p10_us": round(t[len(t) // 10], 2),
+                  "p90_us": round(t[(9 * len(t)) // 10], 2), "samples": len(t)}
+    return out
+
+
+def copy_ceiling(torch, stream, dev, nbytes=2 << 30, rounds=21):
+    """Same-session HBM ceiling: median of `rounds` device-to-device copies of
+    2 GiB (read + write = 4 GiB moved each)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    pairs = []
+    for _ in range(rounds):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e-3 for a, b in pairs)
+    med = t[len(t) // 2]
+    gbs = 2 * nbytes / med / 1e9
+    del src, dst
+    return {"copy_bytes": nbytes, "bytes_moved": 2 * nbytes, "median_us": round(med * 1e6, 1),
+            "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4), "samples": rounds}
+
+
 def build_stack(torch, api, WL, projs, layers, code, ncode, dev, seed0):
     weights = []
     for l in range(layers):
         row = []
         for i, p in enumerate(projs):
-            w = WL.gpu_weight_f32(p.N, p.K, seed=seed0 + l * 16 + i, device=dev)
+            w = WL.gpu_weight_f32(p.N, p.K, seed=WL.stack_weight_seed(seed0, l, i), device=dev)
             row.append(api.nf4_quantize(w, code, ncode))
             del w
         weights.append(row)
@@ -101,14 +164,14 @@ def layer_inputs(torch, WL, projs, layers, M, dev, seed0):
     """One input per producer inside a layer (q/k/v share, gate/up share), a
     grad_y per projection."""
     xs, gys = [], []
-    kdim = {p.name: p.K for p in projs}
+    kdim = {}
+    for i, p in enumerate(projs):
+        kdim.setdefault(WL.X_SLOT[i], p.K)
     for l in range(layers):
-        xa = WL.gpu_normal_bf16(M, kdim["q"], seed=seed0 + 4 * l, device=dev)
-        xo = WL.gpu_normal_bf16(M, kdim["o"], seed=seed0 + 4 * l + 1, device=dev)
-        xm = WL.gpu_normal_bf16(M, kdim["gate"], seed=seed0 + 4 * l + 2, device=dev)
-        xd = WL.gpu_normal_bf16(M, kdim["down"], seed=seed0 + 4 * l + 3, device=dev)
-        xs.append([xa, xa, xa, xo, xm, xm, xd])
-        gys.append([WL.gpu_normal_bf16(M, p.N, seed=seed0 + 10_000 + l * 16 + i, device=dev)
+        ins = {s: WL.gpu_normal_bf16(M, k, seed=WL.stack_x_seed(seed0, l, s), device=dev)
+               for s, k in kdim.items()}
+        xs.append([ins[WL.X_SLOT[i]] for i in range(len(projs))])
+        gys.append([WL.gpu_normal_bf16(M, p.N, seed=WL.stack_gy_seed(seed0, l, i), device=dev)
                     for i, p in enumerate(projs)])
     return xs, gys
 
@@ -139,6 +202,12 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
     projs = WL.LLAMA_8B
     L = len(llama_weights)
     wbytes = sum(w.nbytes() for row in llama_weights for w in row)
+
+    # same-session HBM ceiling, measured first so the decode passes can be set
+    # against it as well as against the 8 TB/s peak
+    ceil = copy_ceiling(torch, stream, dev)
+    extra["hbm_copy_ceiling"] = ceil
+    log(f"copy ceiling: {ceil}")
 
     # decode-size M: forward only over the same 224 weights (3.6 GB, beyond the
     # 256 MB last-level cache)
@@ -173,6 +242,7 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
         gbs = wbytes / (ms * 1e-3) / 1e9
         dec[f"M={M}"] = {"us_per_pass": round(ms * 1e3, 1), "weight_GBps": round(gbs, 1),
                          "frac_of_8TBps": round(gbs / PEAK_HBM_GBS, 4),
+                         "frac_of_copy_ceiling": round(gbs / ceil["GBps"], 4),
                          "graph_replay_bitwise_equal": same,
                          "us_per_pass_eager_launches": round(ms_eager * 1e3, 1)}
         del graph
@@ -184,18 +254,22 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
     # Today's path as the comparator: dequantise every visit, then the dense
     # bf16 GEMM (hipBLASLt through torch), per Llama projection at M = 512 on
     # layer 0's weights; and the dense GEMM alone on a resident dequantised
-    # weight (the same-session dense ceiling).  Outputs are compared with the
-    # fused ones: same exact product, different accumulation order.
+    # weight (the same-session dense ceiling).  The three arms are interleaved
+    # round by round (medians of 21 rounds of 5 calls).  Outputs are compared
+    # with the fused ones: same exact product, different accumulation order.
     import torch.nn.functional as F
+    filler = filler_copy(torch, dev)
+    arm_names = ("fused", "dequant_plus_dense", "dense_only")
     M = WL.LLAMA_M
     comp = {}
-    tot = {"fused_us": 0.0, "dequant_plus_dense_us": 0.0, "dense_only_us": 0.0}
+    tot = {f"{n}_us": 0.0 for n in arm_names}
     for i, p in enumerate(projs):
         w = llama_weights[0][i]
         x = WL.gpu_normal_bf16(M, p.K, seed=90_000 + i, device=dev)
         gy = WL.gpu_normal_bf16(M, p.N, seed=91_000 + i, device=dev)
         ws_c = workspace_for(torch, api, [p], [M], dev)
         wd = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=dev)
+        wd_r = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=dev)
         y_f = torch.empty((M, p.N), dtype=torch.bfloat16, device=dev)
         g_f = torch.empty((M, p.K), dtype=torch.bfloat16, device=dev)
 
@@ -210,14 +284,13 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
             g = torch.matmul(gy, wd)
             return y, g
 
-        api.nf4_dequantize(w, out=wd)
+        api.nf4_dequantize(w, out=wd_r)
 
         def dense():
-            return F.linear(x, wd), torch.matmul(gy, wd)
+            return F.linear(x, wd_r), torch.matmul(gy, wd_r)
 
-        t_f = timed(torch, stream, fused, steps=20, warmup=3) * 1e3
-        t_t = timed(torch, stream, today, steps=20, warmup=3) * 1e3
-        t_d = timed(torch, stream, dense, steps=20, warmup=3) * 1e3
+        med = interleaved(torch, stream, dict(zip(arm_names, (fused, today, dense))), filler)
+        t_f, t_t, t_d = (med[n]["median_us"] for n in arm_names)
         api.nf4_reset_path_counts()
         fused()
         torch.cuda.synchronize()
@@ -234,16 +307,17 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
 
         ry, ey = diff(y_f, y_c)
         rg, eg = diff(g_f, g_c)
-        comp[p.name] = {"fused_us": round(t_f, 1), "dequant_plus_dense_us": round(t_t, 1),
-                        "dense_only_us": round(t_d, 1), "speedup_vs_today": round(t_t / t_f, 2),
+        comp[p.name] = {"fused_us": t_f, "dequant_plus_dense_us": t_t,
+                        "dense_only_us": t_d, "speedup_vs_today": round(t_t / t_f, 2),
+                        "p10_p90_us": {n: [med[n]["p10_us"], med[n]["p90_us"]] for n in arm_names},
                         "fwd_rel_fro_diff": float(f"{ry:.3g}"), "fwd_identical_frac": round(ey, 4),
                         "bwd_rel_fro_diff": float(f"{rg:.3g}"), "bwd_identical_frac": round(eg, 4),
                         "fused_kernels_ran": ran_fused}
-        tot["fused_us"] += t_f
-        tot["dequant_plus_dense_us"] += t_t
-        tot["dense_only_us"] += t_d
-        del x, gy, ws_c, wd, y_f, g_f, y_c, g_c
+        for n, t in zip(arm_names, (t_f, t_t, t_d)):
+            tot[f"{n}_us"] += t
+        del x, gy, ws_c, wd, wd_r, y_f, g_f, y_c, g_c
     flops_layer = 2 * sum(2.0 * M * p.N * p.K for p in projs)
+    comp["timing"] = "per arm: median over 21 interleaved rounds of 5 calls, each round after a 1 GiB filler copy"
     comp["layer_total"] = {k: round(v, 1) for k, v in tot.items()}
     comp["layer_total"]["fused_tflops"] = round(flops_layer / (tot["fused_us"] * 1e-6) / 1e12, 1)
     comp["layer_total"]["dense_only_tflops"] = round(flops_layer / (tot["dense_only_us"] * 1e-6) / 1e12, 1)
@@ -251,30 +325,34 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
     # decode sizes, forward only: the streaming kernel against dequantise +
     # dense GEMV/GEMM, summed over layer 0's seven projections
     for Md in WL.DECODE_MS:
-        t = {"fused_us": 0.0, "dequant_plus_dense_us": 0.0, "dense_only_us": 0.0}
+        t = {f"{n}_us": 0.0 for n in arm_names}
         rels, ran = [], True
         for i, p in enumerate(projs):
             w = llama_weights[0][i]
             x = WL.gpu_normal_bf16(Md, p.K, seed=92_000 + i, device=dev)
             ws_c = workspace_for(torch, api, [p], [Md], dev)
             wd = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=dev)
+            wd_r = torch.empty((p.N, p.K), dtype=torch.bfloat16, device=dev)
+            api.nf4_dequantize(w, out=wd_r)
             y_f = torch.empty((Md, p.N), dtype=torch.bfloat16, device=dev)
-            t["fused_us"] += timed(torch, stream, lambda: api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c),
-                                   steps=20, warmup=3) * 1e3
-            t["dequant_plus_dense_us"] += timed(
-                torch, stream, lambda: F.linear(x, api.nf4_dequantize(w, out=wd)), steps=20, warmup=3) * 1e3
-            t["dense_only_us"] += timed(torch, stream, lambda: F.linear(x, wd), steps=20, warmup=3) * 1e3
+            med = interleaved(torch, stream, {
+                "fused": lambda: api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c),
+                "dequant_plus_dense": lambda: F.linear(x, api.nf4_dequantize(w, out=wd)),
+                "dense_only": lambda: F.linear(x, wd_r)}, filler)
+            for n in arm_names:
+                t[f"{n}_us"] += med[n]["median_us"]
             api.nf4_reset_path_counts()
             api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c)
-            y_c = F.linear(x, wd)
+            y_c = F.linear(x, wd_r)
             torch.cuda.synchronize()
             ran = ran and api.nf4_path_counts()["fwd_small_m"] == 1
             rels.append(float((y_f.float() - y_c.float()).norm().item() / max(y_c.float().norm().item(), 1e-30)))
-            del x, ws_c, wd, y_f, y_c
+            del x, ws_c, wd, wd_r, y_f, y_c
         comp[f"decode_M={Md}_fwd"] = {k: round(v, 1) for k, v in t.items()}
         comp[f"decode_M={Md}_fwd"].update({
             "speedup_vs_today": round(t["dequant_plus_dense_us"] / t["fused_us"], 2),
             "max_rel_fro_diff": float(f"{max(rels):.3g}"), "fused_kernels_ran": ran})
+    del filler
     extra["comparator_llama8b_layer0"] = comp
     log(f"comparator done: {comp['layer_total']}")
 
@@ -406,11 +484,24 @@ def run_streaming(torch, api, WL, dev, llama_weights, stream, slots=3):
 
 
 # ---------------------------------------------------------------------------
+def _repeat(fn, min_s, max_reps):
+    """Run fn until at least min_s seconds have passed (at most max_reps times)."""
+    reps = 0
+    t0 = time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_s):
+        fn()
+        reps += 1
+    return reps, time.perf_counter() - t0
+
+
 def cpu_baseline(WL):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    layer 0 of the Llama-3.1-8B stack at M = 512, all 7 projections, each
-    dequantised from its packed NF4 form and multiplied forward and backward
-    (the oracle's fp64 matmul).  Quantisation is set-up and not timed."""
+    """The CPU oracle, as it stands, on bounded samples of the workloads:
+    the headline figure is layer 0 of the Llama-3.1-8B stack at M = 512, all 7
+    projections, each dequantised from its packed NF4 form and multiplied
+    forward and backward (the oracle's fp64 matmul); "breadth" times the same
+    oracle on the tiny linear, on decode (M = 1), on one Qwen-32B projection
+    at M = 2048 and on 8 of the 64 OLMoE experts.  Quantisation is set-up and
+    not timed."""
     import numpy as np
     from oracle import nf4_oracle as O
 
@@ -420,9 +511,15 @@ def cpu_baseline(WL):
         threads = max((d.get("num_threads") or 0) for d in threadpool_info()) or None
     except Exception:
         pass
+    code, ncode = WL.nf4_code_np(), WL.nested_code_np()
+
+    def deq(q, shape, nested=True):
+        return O.dequantize_nf4_bf16_bits(q["packed"], q["absmax"], q["nested_absmax"] if nested else None,
+                                          q["nested_offset"] if nested else None, code,
+                                          ncode if nested else None).reshape(shape)
+
     projs = WL.LLAMA_8B
     M = WL.LLAMA_M
-    code, ncode = WL.nf4_code_np(), WL.nested_code_np()
     qs = []
     for i, p in enumerate(projs):
         w = WL.weight_f32(p.N, p.K, WL.W_LLAMA, 0, i)
@@ -430,69 +527,177 @@ def cpu_baseline(WL):
         del w
     x = {p.K: WL.bf16_bits(WL.x_bf16(M, p.K, WL.W_LLAMA, 0)) for p in projs}
     gy = [WL.bf16_bits(WL.grad_y_bf16(M, p.N, WL.W_LLAMA, 0, i)) for i, p in enumerate(projs)]
-    # repeat the layer pass until at least 10 s of CPU work (at most 8 passes)
-    passes = 0
-    t0 = time.perf_counter()
-    while passes < 8 and (passes == 0 or time.perf_counter() - t0 < 10.0):
+
+    def layer_pass():
         for i, p in enumerate(projs):
-            q = qs[i]
-            wb = O.dequantize_nf4_bf16_bits(q["packed"], q["absmax"], q["nested_absmax"],
-                                            q["nested_offset"], code, ncode).reshape(p.N, p.K)
+            wb = deq(qs[i], (p.N, p.K))
             O.matmul_fwd(x[p.K], wb)
             O.matmul_bwd_input(gy[i], wb)
-        passes += 1
-    dt = time.perf_counter() - t0
+
+    passes, dt = _repeat(layer_pass, 6.0, 8)
     flops = passes * 2 * sum(2.0 * M * p.N * p.K for p in projs)
+    breadth = {}
+
+    # tiny linear: M = 64, N = 128, K = 256, plain NF4
+    wt = WL.weight_f32(WL.TINY_N, WL.TINY_K, WL.W_TINY, 0)
+    qt = O.quantize_nf4(wt, code)
+    xt = WL.bf16_bits(WL.x_bf16(WL.TINY_M, WL.TINY_K, WL.W_TINY, 0))
+    gt = WL.bf16_bits(WL.grad_y_bf16(WL.TINY_M, WL.TINY_N, WL.W_TINY, 0))
+
+    def tiny():
+        wb = deq(qt, (WL.TINY_N, WL.TINY_K), nested=False)
+        O.matmul_fwd(xt, wb)
+        O.matmul_bwd_input(gt, wb)
+
+    n, t = _repeat(tiny, 0.5, 10_000)
+    breadth["tiny_linear"] = {"value": round(n * 2 * 2.0 * WL.TINY_M * WL.TINY_N * WL.TINY_K / t / 1e9, 4),
+                              "unit": "GFLOP/s", "seconds": round(t, 2),
+                              "sample": f"M=64 N=128 K=256 plain NF4, {n} passes of dequantise + fwd + bwd_input"}
+
+    # decode: layer 0's attention projections (q, k, v, o) forward at M = 1,
+    # rated on their packed weight bytes
+    x1 = {p.K: WL.bf16_bits(WL.x_bf16(1, p.K, WL.W_DECODE, 0)) for p in projs[:4]}
+
+    def decode():
+        for i, p in enumerate(projs[:4]):
+            O.matmul_fwd(x1[p.K], deq(qs[i], (p.N, p.K)))
+
+    n, t = _repeat(decode, 0.0, 1)
+    wbytes = sum(O.storage_bytes(p.N * p.K, True) for p in projs[:4])
+    breadth["decode_m1"] = {"value": round(n * wbytes / t / 1e9, 4), "unit": "GB/s of packed weights",
+                            "seconds": round(t, 2),
+                            "sample": "Llama-3.1-8B layer 0 q/k/v/o at M=1, 1 pass of dequantise + fwd"}
+
+    # Qwen-32B q projection (5120 x 5120) at M = 2048, forward and backward
+    qp = WL.QWEN_32B[0]
+    wq = WL.weight_f32(qp.N, qp.K, WL.W_QWEN, 0, 0)
+    qq = O.quantize_nf4(wq, code, ncode, nested=True)
+    del wq
+    xq = WL.bf16_bits(WL.x_bf16(WL.QWEN_M, qp.K, WL.W_QWEN, 0))
+    gq = WL.bf16_bits(WL.grad_y_bf16(WL.QWEN_M, qp.N, WL.W_QWEN, 0, 0))
+
+    def qwen():
+        wb = deq(qq, (qp.N, qp.K))
+        O.matmul_fwd(xq, wb)
+        O.matmul_bwd_input(gq, wb)
+
+    n, t = _repeat(qwen, 0.0, 1)
+    breadth["qwen32b_q_m2048"] = {"value": round(n * 2 * 2.0 * WL.QWEN_M * qp.N * qp.K / t / 1e12, 5),
+                                  "unit": "TFLOP/s", "seconds": round(t, 2),
+                                  "sample": "Qwen-32B q projection at M=2048, 1 pass of dequantise + fwd + bwd_input"}
+
+    # OLMoE: experts 0..7 of the gate, up and down stacks with their routed rows
+    E8, H, I = 8, WL.OLMOE_HIDDEN, WL.OLMOE_INTER
+    _, _, offsets = WL.olmoe_routing()
+    off8 = offsets[:E8 + 1].astype(np.int32)
+    T8 = int(off8[-1])
+    stacks = []
+    for j, (N, K) in enumerate(((I, H), (I, H), (H, I))):
+        w8 = WL.weight_f32(E8 * N, K, WL.W_OLMOE, 0, j)
+        stacks.append((O.quantize_nf4(w8, code, ncode, nested=True), N, K,
+                       WL.bf16_bits(WL.x_bf16(T8, K, WL.W_OLMOE, 0, j)),
+                       WL.bf16_bits(WL.grad_y_bf16(T8, N, WL.W_OLMOE, 0, j))))
+        del w8
+
+    def olmoe():
+        for q, N, K, xe, ge in stacks:
+            wb = deq(q, (E8, N, K))
+            O.grouped_matmul_fwd(xe, off8, wb)
+            O.grouped_matmul_bwd_input(ge, off8, wb)
+
+    n, t = _repeat(olmoe, 0.0, 1)
+    fl = sum(2 * 2.0 * T8 * N * K for _, N, K, _, _ in stacks)
+    breadth["olmoe_8_experts"] = {"value": round(n * fl / t / 1e12, 5), "unit": "TFLOP/s",
+                                  "seconds": round(t, 2),
+                                  "sample": f"OLMoE gate/up/down experts 0-7 ({T8} routed rows), 1 pass of "
+                                            f"dequantise + grouped fwd + grouped bwd_input"}
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
             "cores": threads or len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"Llama-3.1-8B layer 0 (7 projections) at M=512, {passes} pass(es): dequantise "
                       f"+ fwd + bwd_input, NumPy oracle (fp64 matmul)",
-            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": round(dt, 2), "host_cpus": len(os.sched_getaffinity(0)),
+            "breadth": breadth}
 
 
 # ---------------------------------------------------------------------------
 def run_only(args):
-    """One shape of the step: the 32 layers' launches of one projection in one
-    direction (distinct weights, as in the step), `steps` times."""
+    """One shape of a workload, launched with distinct weights per call as in
+    the step, `steps` times.  FAMILY:DIR_PROJ names it: llama:fwd_gate (the
+    32 layers' forward gate projections of the M = 512 step; "llama:" may be
+    left out), qwen:bwd_down (8 distinct Qwen-32B down weights at M = 2048),
+    olmoe:fwd_gate (4 distinct copies of the OLMoE gate expert stack, grouped
+    call over the 4096 routed rows)."""
     import torch
 
     import workloads as WL
     from nf4_bit_weight_amd import api
 
-    d, name = args.only.split("_", 1)
-    projs = WL.LLAMA_8B
-    i = [p.name for p in projs].index(name)
-    p = projs[i]
-    M, L = (args.m or WL.LLAMA_M), WL.LLAMA_LAYERS
+    family, _, shape = args.only.rpartition(":")
+    family = family or "llama"
+    d, name = shape.split("_", 1)
+    if d not in ("fwd", "bwd") or family not in ("llama", "qwen", "olmoe"):
+        raise SystemExit(f"--only {args.only}: expected [llama:|qwen:|olmoe:](fwd|bwd)_<projection>")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     code = torch.from_numpy(WL.nf4_code_np()).to(dev)
     ncode = torch.from_numpy(WL.nested_code_np()).to(dev)
-    ws_ = []
-    for l in range(L):
-        w = WL.gpu_weight_f32(p.N, p.K, seed=10_000 + l * 16 + i, device=dev)
-        ws_.append(api.nf4_quantize(w, code, ncode))
-        del w
-    ins = [WL.gpu_normal_bf16(M, p.K if d == "fwd" else p.N, seed=30_000 + l, device=dev) for l in range(L)]
-    out = torch.empty((M, p.N if d == "fwd" else p.K), dtype=torch.bfloat16, device=dev)
-    ws = workspace_for(torch, api, [p], [M], dev)
+    off = None
+    if family == "olmoe":
+        E, H, I = WL.OLMOE_E, WL.OLMOE_HIDDEN, WL.OLMOE_INTER
+        dims = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+        N, K = dims[name]
+        j = list(dims).index(name)
+        _, _, offsets = WL.olmoe_routing()
+        off = torch.from_numpy(offsets).to(dev)
+        M, L = int(offsets[-1]), 4
+        wts = []
+        for l in range(L):
+            w = WL.gpu_weight_f32(E * N, K, seed=70_000 + 16 * l + j, device=dev)
+            wts.append(api.nf4_quantize(w, code, ncode).per_expert(E))
+            del w
+    else:
+        projs = WL.LLAMA_8B if family == "llama" else WL.QWEN_32B
+        i = [p.name for p in projs].index(name)
+        N, K = projs[i].N, projs[i].K
+        if family == "llama":
+            M, L, seed0 = (args.m or WL.LLAMA_M), WL.LLAMA_LAYERS, 10_000
+        else:
+            M, L, seed0 = (args.m or WL.QWEN_M), 8, 50_000
+        wts = []
+        for l in range(L):
+            w = WL.gpu_weight_f32(N, K, seed=WL.stack_weight_seed(seed0, l, i), device=dev)
+            wts.append(api.nf4_quantize(w, code, ncode))
+            del w
+    ins = [WL.gpu_normal_bf16(M, K if d == "fwd" else N, seed=30_000 + l, device=dev) for l in range(L)]
+    out = torch.empty((M, N if d == "fwd" else K), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(16, api.nf4_workspace_bytes(1, M, N, K), api.nf4_workspace_bytes(2, M, N, K)),
+                     dtype=torch.uint8, device=dev)
 
     def one():
         for l in range(L):
-            if d == "fwd":
-                api.nf4_matmul_fwd(ins[l], ws_[l], out=out, ws=ws)
+            if off is not None:
+                if d == "fwd":
+                    api.nf4_grouped_matmul_fwd(ins[l], off, wts[l], WL.OLMOE_E, out=out)
+                else:
+                    api.nf4_grouped_matmul_bwd_input(ins[l], off, wts[l], WL.OLMOE_E, out=out)
+            elif d == "fwd":
+                api.nf4_matmul_fwd(ins[l], wts[l], out=out, ws=ws)
             else:
-                api.nf4_matmul_bwd_input(ins[l], ws_[l], out=out, ws=ws)
+                api.nf4_matmul_bwd_input(ins[l], wts[l], out=out, ws=ws)
 
     ms = timed(torch, stream, one, args.steps, args.warmup) / L
-    flops = 2.0 * M * p.N * p.K
+    flops = 2.0 * M * N * K
+    wbytes = wts[0].nbytes()
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-    print(json.dumps({"shape": args.only, "M": M, "N": p.N, "K": p.K, "ops": L * (args.steps + args.warmup),
-                      "avg_us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+    print(json.dumps({"shape": f"{family}:{shape}", "M": M, "N": N, "K": K,
+                      "experts": WL.OLMOE_E if off is not None else None,
+                      "ops": L * (args.steps + args.warmup), "avg_us": round(ms * 1e3, 2),
+                      "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                      "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1),
                       "copy_bytes": args.copy_bytes}), flush=True)
 
 
@@ -524,8 +729,8 @@ def main():
     M, L, projs = WL.LLAMA_M, WL.LLAMA_LAYERS, WL.LLAMA_8B
     t0 = time.time()
     log("building the 32-layer Llama-3.1-8B NF4 stack")
-    weights = build_stack(torch, api, WL, projs, L, code, ncode, dev, seed0=10_000)
-    xs, gys = layer_inputs(torch, WL, projs, L, M, dev, seed0=20_000)
+    weights = build_stack(torch, api, WL, projs, L, code, ncode, dev, seed0=WL.LLAMA_STACK_W_SEED)
+    xs, gys = layer_inputs(torch, WL, projs, L, M, dev, seed0=WL.LLAMA_STACK_IN_SEED)
     ys = [torch.empty((M, p.N), dtype=torch.bfloat16, device=dev) for p in projs]
     gxs = [torch.empty((M, p.K), dtype=torch.bfloat16, device=dev) for p in projs]
     ws = workspace_for(torch, api, projs, [M], dev)

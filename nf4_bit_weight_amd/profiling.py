@@ -10,12 +10,19 @@ HBM-traffic figure back for the benchmark line.  Needs no GPU.
     python -m nf4_bit_weight_amd.profiling mfma <counter_collection.csv> <flops_per_op>
            <out.md> "<shape>" "<command>"
     python -m nf4_bit_weight_amd.profiling lds <counter_collection.csv> <out.md> "<shape>" "<command>"
+    python -m nf4_bit_weight_amd.profiling counters <counter_collection.csv> <copy_bytes> <ops>
+           <bytes_per_op> <out.md> "<shape>" "<command>"
 
 MFMA: one rocprofv3 run collecting the derived MfmaUtil and VALUBusy metrics
 (percent of the dispatch's active cycles in which the MFMA unit, resp. the
 vector ALU, was busy, averaged over SIMDs / CUs) and SQ_INSTS_VALU_MFMA_MOPS_BF16
 (bf16 MFMA work in units of 512 flops), averaged over the fused matmul
 dispatches; the counted flops are checked against 2 M N K.
+
+Counters: every counter of one run summed over the fused dispatches and
+divided by the operations; FETCH_SIZE / WRITE_SIZE also in bytes, scaled by
+the calibration copy as below, and set against the algorithmic bytes of one
+operation (the decode runs: FETCH_SIZE with SQ_INSTS_VALU and GRBM_GUI_ACTIVE).
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one rocprofv3 run
 each) summed over the dispatches of the measured operation (the fused GEMM
@@ -36,8 +43,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/nf4_gemm.hip", "csrc/nf4_gemv.hip", "csrc/nf4_device.hpp")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_splitk_reduce")
-MFMA_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<")
+FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_gemv_ln<", "k_gemm8<", "k_splitk_reduce")
+MFMA_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_gemv_ln<", "k_gemm8<")
 
 
 def _code_only(text: str) -> str:
@@ -263,6 +270,61 @@ def summarize_lds(pmc_csv, out_md, shape, command) -> dict:
     return fig
 
 
+def counter_figures(pmc_csv: str, copy_bytes: int, ops: int, bytes_per_op: float) -> dict:
+    names = sorted({r["Counter_Name"] for r in csv.DictReader(open(pmc_csv))})
+    res = {"per_op": {}}
+    kernels = set()
+    for c in names:
+        disp = _per_dispatch(pmc_csv, c)
+        fused = [(n, v) for (n, v) in disp.values() if any(k in n for k in FUSED_KERNELS)]
+        if not fused:
+            raise RuntimeError(f"{pmc_csv}: no fused-kernel dispatches for {c}")
+        kernels.update(_short(n) for n, _ in fused)
+        res["fused_dispatches"] = len(fused)
+        res["per_op"][c] = round(sum(v for _, v in fused) / ops, 1)
+        if c in ("FETCH_SIZE", "WRITE_SIZE"):
+            copies = [v for (n, v) in disp.values() if COPY_KERNEL in n]
+            if not copies:
+                raise RuntimeError(f"{pmc_csv}: no calibration copy for {c}")
+            factor = (copy_bytes / 1024.0) / max(copies)
+            res[f"{c}_factor"] = round(factor, 4)
+            res[f"{c}_bytes_per_op"] = round(res["per_op"][c] * 1024.0 * factor)
+            if bytes_per_op:
+                res[f"{c}_over_algorithmic"] = round(res[f"{c}_bytes_per_op"] / bytes_per_op, 4)
+    res["kernels"] = sorted(kernels)
+    res["algorithmic_bytes_per_op"] = round(bytes_per_op)
+    return res
+
+
+def summarize_counters(pmc_csv, copy_bytes, ops, bytes_per_op, out_md, shape, command) -> dict:
+    fig = counter_figures(pmc_csv, int(copy_bytes), int(ops), float(bytes_per_op))
+    fig["shape"] = shape
+    fig["ops"] = int(ops)
+    fig["copy_bytes"] = int(copy_bytes)
+    fig["kernel_source_sha256"] = kernel_source_sha256()
+    lines = [
+        f"# Counters of the fused NF4 kernels: {shape}",
+        "",
+        "One rocprofv3 counter run of:",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"per_op: each counter summed over the fused dispatches and divided by the {ops} operations. "
+        f"FETCH_SIZE (KiB) is scaled to bytes by the factor that maps it onto a plain {copy_bytes} B "
+        f"device copy (`{COPY_KERNEL}`) in the same run. SQ_INSTS_VALU counts wave-level VALU "
+        "instructions (MFMA included); GRBM_GUI_ACTIVE counts GPU-busy cycles of the dispatches.",
+        "",
+        "```json",
+        json.dumps(fig, indent=1),
+        "```",
+    ]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return fig
+
+
 def read_traffic(md_path: str):
     """The figures of a traffic summary, or None when the file is missing or
     was measured on other kernel sources."""
@@ -286,6 +348,9 @@ def main(argv):
         print(json.dumps(summarize_lds(argv[1], argv[2], argv[3], argv[4])))
     elif len(argv) >= 6 and argv[0] == "mfma":
         print(json.dumps(summarize_mfma(argv[1], float(argv[2]), argv[3], argv[4], argv[5])))
+    elif len(argv) >= 8 and argv[0] == "counters":
+        print(json.dumps(summarize_counters(argv[1], int(argv[2]), int(argv[3]), float(argv[4]),
+                                            argv[5], argv[6], argv[7])))
     elif len(argv) >= 8 and argv[0] == "traffic":
         fig = summarize_traffic(argv[1], argv[2], int(argv[3]), int(argv[4]), argv[5], argv[6], argv[7])
         print(json.dumps(fig))

@@ -185,4 +185,4 @@ def test_llama_projection_m512(idx):
 
 @pytest.mark.parametrize("idx", [0, 1, 4, 6])          # q/o, k/v, gate/up, down: each distinct shape
 def test_qwen_projection_m2048(idx):
-    _full_size(WL.QWEN_32B, idx, WL.QWEN_M, WL.W_QWEN, sample_rows=32)
+    _full_size(WL.QWEN_32B, idx, WL.QWEN_M, WL.W_QWEN, sample_rows=64)   # 8 per 256-row tile

@@ -162,6 +162,26 @@ def olmoe_routing(tokens: int = OLMOE_TOKENS, experts: int = OLMOE_E, topk: int 
     return tok[perm], exp[perm], offsets
 
 
+# Seeds of the 32-layer stacks the benchmark draws on the device: the weight
+# of projection i in layer l, the layer's inputs (q/k/v read one input,
+# gate/up another; X_SLOT maps a projection to its input) and one grad_y per
+# projection.
+LLAMA_STACK_W_SEED, LLAMA_STACK_IN_SEED = 10_000, 20_000
+X_SLOT = (0, 0, 0, 1, 2, 2, 3)
+
+
+def stack_weight_seed(seed0: int, layer: int, i: int) -> int:
+    return seed0 + 16 * layer + i
+
+
+def stack_x_seed(seed0: int, layer: int, slot: int) -> int:
+    return seed0 + 4 * layer + slot
+
+
+def stack_gy_seed(seed0: int, layer: int, i: int) -> int:
+    return seed0 + 10_000 + 16 * layer + i
+
+
 def gpu_weight_f32(N: int, K: int, seed: int, device="cuda", std: float = 0.02) -> torch.Tensor:
     """W [N, K] fp32 ~ std * N(0, 1) drawn on the device by torch's seeded
     Philox generator (used where host draws would be too slow: the 32-layer
