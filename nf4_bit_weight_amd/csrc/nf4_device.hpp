@@ -103,6 +103,28 @@ __device__ __forceinline__ void expand8(uint32_t p, const Lut& t, uint32_t (&out
   out[3] = perm(o23, e23, 0x07060302u);                // (w6, w7)
 }
 
+// Expand 8 nibbles in the order (0, 2, 4, 6, 1, 3, 5, 7): out[0] = (w0, w2),
+// out[1] = (w4, w6), out[2] = (w1, w3), out[3] = (w5, w7).  Four byte
+// permutations fewer than expand8; the other operand of the product is read
+// in the same order (both sides of a dot product may permute their terms
+// alike), or, where the expanded index is an output column, the column is
+// mapped back when the result is written.
+__device__ __forceinline__ void expand8_eo(uint32_t p, const Lut& t, uint32_t (&out)[4]) {
+  const uint32_t se = (p >> 4) & 0x07070707u;
+  const uint32_t so = p & 0x07070707u;
+  const uint32_t me = perm(p, p << 8, 0x0B090A08u);
+  const uint32_t p4 = p << 4;
+  const uint32_t mo = perm(p4, p4 << 8, 0x0B090A08u);
+  const uint32_t he = bitsel(me, perm(t.h[3], t.h[2], se), perm(t.h[1], t.h[0], se));
+  const uint32_t le = bitsel(me, perm(t.l[3], t.l[2], se), perm(t.l[1], t.l[0], se));
+  const uint32_t ho = bitsel(mo, perm(t.h[3], t.h[2], so), perm(t.h[1], t.h[0], so));
+  const uint32_t lo = bitsel(mo, perm(t.l[3], t.l[2], so), perm(t.l[1], t.l[0], so));
+  out[0] = perm(he, le, 0x05010400u);
+  out[1] = perm(he, le, 0x07030602u);
+  out[2] = perm(ho, lo, 0x05010400u);
+  out[3] = perm(ho, lo, 0x07030602u);
+}
+
 // Decoded scale of block b.  `ncode` is the 256-entry nested table (LDS or
 // global), `absmax` is u8 in the nested form and f32 otherwise.
 template <bool NESTED>

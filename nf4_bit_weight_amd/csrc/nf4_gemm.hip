@@ -175,23 +175,45 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // array cannot index out of range); the tile stops at its expert's last row
 // and meets that expert's slice of the [E * N, K] stack.  Returns false for a
 // tile id past the last expert's tiles (m_tiles is an upper bound).
+//
+// Grouped search: 64 experts per round, one per lane of the wave: the lanes
+// load their offsets together, an inclusive prefix sum of the tile counts
+// runs across the wave, and a ballot names the expert whose tiles contain
+// mt.  Every wave of the workgroup reaches the same answer on its own (no
+// LDS, no barrier); called by whole waves.
 template <int BM, bool GROUPED>
 __device__ __forceinline__ bool row_tile(const GemmParams& p, int mt, int64_t N, int64_t& row0,
                                          int64_t& row_end, int64_t& wrow_base) {
   if constexpr (GROUPED) {
-    int acc = 0;
-    for (int e = 0; e < p.E; ++e) {
-      int64_t a = p.offsets[e], b = p.offsets[e + 1];
-      a = a < 0 ? 0 : (a > p.M ? p.M : a);
-      b = b < a ? a : (b > p.M ? p.M : b);
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    int acc = 0;                                   // tiles of the experts before this round
+    for (int e0 = 0; e0 < p.E; e0 += 64) {
+      const int e = e0 + lane;
+      int64_t a = 0, b = 0;
+      if (e < p.E) {
+        a = p.offsets[e];
+        b = p.offsets[e + 1];
+        a = a < 0 ? 0 : (a > p.M ? p.M : a);
+        b = b < a ? a : (b > p.M ? p.M : b);
+      }
       const int cnt = static_cast<int>((b - a + BM - 1) / BM);
-      if (mt < acc + cnt) {
-        row0 = a + static_cast<int64_t>(mt - acc) * BM;
-        row_end = b;
-        wrow_base = static_cast<int64_t>(e) * N;
+      int incl = cnt;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+      }
+      const int lo = acc + incl - cnt;             // first tile of expert e
+      const unsigned long long hit = __ballot(mt >= lo && mt < acc + incl);
+      if (hit != 0) {
+        const int l = __ffsll(static_cast<long long>(hit)) - 1;
+        const int first = __shfl(lo, l, 64);
+        row0 = __shfl(a, l, 64) + static_cast<int64_t>(mt - first) * BM;
+        row_end = __shfl(b, l, 64);
+        wrow_base = static_cast<int64_t>(e0 + l) * N;
         return true;
       }
-      acc += cnt;
+      acc += __shfl(incl, 63, 64);
     }
     return false;
   } else {
@@ -1447,44 +1469,60 @@ __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restr
 }
 
 // ---------------------------------------------------------------------------------
-// 8-bit blockwise fused GEMM: forward and input gradient, plain and grouped.
+// Register-staged tile kernel: the 8-bit blockwise formats, and NF4 tiles of
+// 32 to 128 rows (grouped experts, small products).
 //
-// The weight is one index per byte into a 256-entry table (bitsandbytes fork
-// PR "Experts trainability ... ExpertsNbit", "Commit 1": int8 and fp8 e4m3
-// blockwise beside nf4 / fp4), w_hat = bf16(fp32(code[q] * absmax_hat)) with
-// the same 64-element blocks and (nested) scales.  A 256-entry table per
-// (row, block) does not fit the register byte tables of the 4-bit kernels, so
-// the table itself (256 fp32) sits in LDS and each weight costs one LDS
-// lookup, one fp32 multiply and half a packed bf16 conversion.
+// 8-bit: the weight is one index per byte into a 256-entry table
+// (bitsandbytes fork PR "Experts trainability ... ExpertsNbit", "Commit 1":
+// int8 and fp8 e4m3 blockwise beside nf4 / fp4), w_hat =
+// bf16(fp32(code[q] * absmax_hat)) with the same 64-element blocks and
+// (nested) scales.  A 256-entry table per (row, block) does not fit the
+// register byte tables, so the table (256 fp32) sits in LDS and each weight
+// costs one LDS lookup, one fp32 multiply and half a packed conversion.
+// NF4: each thread expands one whole (row, 64-block) per step through the
+// register byte tables (one table per block), in the (0,2,4,6,1,3,5,7) order
+// of expand8_eo; the forward stores its activation tile in the same order,
+// the input gradient maps the output column back in the epilogue.
 //
-// Tile BM x 128 (BM = 128, or 32 for M <= 32 where it streams the weights
-// once with the contraction split across workgroups), BK = 64, four waves
-// (2 x 2 of 64 x 64, or 1 x 4 of 32 x 32), v_mfma_f32_32x32x16_bf16.  Every
-// step the threads load the next step's activation vectors and 32 weight
-// bytes each into registers, the waves multiply the current LDS buffers, and
-// the threads then store the activations and expand their 32 weights into the
-// other buffer; one barrier per step.  Both LDS tiles are stored
-// [output-or-activation row][contraction] with rows of 64 + 8 elements, so
-// every MFMA fragment is one 16-byte read: the forward expands 32 contiguous
-// contraction elements of one W row, the input gradient 32 output columns
-// of one W row (stored one element per column row).
-template <int BM>
-struct G8 {
-  static constexpr int BN = 128, BK = 64, kPitch = BK + 8;
-  static constexpr int WAVES_M = BM == 128 ? 2 : 1, WAVES_N = 4 / WAVES_M;
+// Tile BM x 128 (BM = 128, 64 or 32), BK = 64 (8-bit) or 128 (NF4): every
+// thread owns 32 weight bytes of a step.  Four waves (2 x 2 of 64 x 64, or
+// 1 x 4 of BM x 32), v_mfma_f32_32x32x16_bf16.  Every step the threads load
+// the next step's activation vectors and weight bytes into registers, the
+// waves multiply the current LDS buffers, and the threads then store the
+// activations and expand their weights into the other buffer; one barrier
+// per step.  A tile and the forward's weight tile are stored [row][BK + 8],
+// so every MFMA fragment is one 16-byte read; the 8-bit input gradient
+// stores its weights one element per output-column row, the NF4 input
+// gradient [contraction][128 + 16] (whole 16-byte stores), read with
+// ds_read_b64_tr_b16 as in the producer/consumer kernel.
+template <int BITS, int BM, int NW>
+struct GT {
+  static_assert(NW == 4 || (NW == 8 && BITS == 4 && BM >= 64), "8 waves: NF4, 64 or 128 rows");
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int BN = 128, BK = BITS == 8 ? 64 : 128, kPitch = BK + 8, kPitchT = BN + 16;
+  static constexpr int WAVES_M = (BM == 128 || NW == 8) ? 2 : 1, WAVES_N = NW / WAVES_M;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int MI = WM / 32, NI = WN / 32;
-  static constexpr int kA = BM * kPitch, kB = BN * kPitch;     // elements per buffer
-  static constexpr int kAVec = BM * BK / 8 / 256;              // 16-byte activation vectors per thread
-  static constexpr int kLds = 2 * (kA + kB) * 2;
+  // weights per thread piece: 32 bytes (4 waves), 16 bytes of NF4 (8 waves)
+  static constexpr int PW = BITS == 8 ? 32 : (NW == 8 ? 32 : 64);
+  static constexpr int kUnits = PW * BITS / 32;                // packed dwords per piece
+  static constexpr int kVR = BK / 8;                           // 16-byte activation vectors per row
+  static constexpr int kA = BM * kPitch;                       // elements per buffer
+  static constexpr int kAVec = BM * BK / 8 / kThreads;         // activation vectors per thread
+  static constexpr int kDepth = 4;                             // steps held in registers
+  static constexpr bool kTrRead(bool trans) { return BITS == 4 && trans; }
+  static constexpr int kB(bool trans) { return kTrRead(trans) ? BK * kPitchT : BN * kPitch; }
+  static constexpr int kLds(bool trans) { return 2 * (kA + kB(trans)) * 2; }
 };
 
-template <int BM, bool TRANS, bool NESTED, bool GROUPED>
-__global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
-  using G = G8<BM>;
-  constexpr int BN = G::BN, BK = G::BK, P = G::kPitch;
+template <int BITS, int BM, int NW, bool TRANS, bool NESTED, bool GROUPED>
+__global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
+  using G = GT<BITS, BM, NW>;
+  constexpr int BN = G::BN, BK = G::BK, P = G::kPitch, PT = G::kPitchT;
+  constexpr bool TR = G::kTrRead(TRANS);
+  constexpr int KB = G::kB(TRANS);
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  __shared__ float scode[256];
+  __shared__ float scode[BITS == 8 ? 256 : 1];
   __shared__ float sncode[256];
 
   const int tid = threadIdx.x;
@@ -1505,36 +1543,47 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
   const int ke = static_cast<int>(static_cast<int64_t>(z + 1) * ktiles / p.splits);
   const int n = ke - kb;
 
-  scode[tid] = p.w.code[tid];
-  if constexpr (NESTED) sncode[tid] = p.w.ncode[tid];
+  float code[BITS == 4 ? 16 : 1];
+  if constexpr (BITS == 8) {
+    if (tid < 256) scode[tid] = p.w.code[tid];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = p.w.code[i];
+  }
+  if constexpr (NESTED) {
+    if (tid < 256) sncode[tid] = p.w.ncode[tid];
+  }
   const float off = NESTED ? p.w.nested_offset[0] : 0.f;
 
   auto a_buf = [&](int b) { return lds + b * G::kA; };
-  auto b_buf = [&](int b) { return lds + 2 * G::kA + b * G::kB; };
+  auto b_buf = [&](int b) { return lds + 2 * G::kA + b * KB; };
 
   // ---- this thread's loads ---------------------------------------------------------
-  // activation vector j: row (tid + 256 j) / 8, 16-byte unit (tid + 256 j) % 8;
-  // rows past the end repeat the last row, columns past Kc repeat the last
-  // vector (they meet zero weights or are never stored)
+  // activation vector j: row (tid + T j) / kVR, 16-byte unit (tid + T j) %
+  // kVR (T threads); rows past the end repeat the last row, columns past Kc
+  // repeat the last vector (they meet zero weights or are never stored)
   const uint16_t* a_row[G::kAVec];
   int a_c8[G::kAVec], a_dst[G::kAVec];
 #pragma unroll
   for (int j = 0; j < G::kAVec; ++j) {
-    const int u = tid + 256 * j;
-    const int r = u >> 3;
+    const int u = tid + G::kThreads * j;
+    const int r = u / G::kVR;
     int64_t row = row0 + r;
     row = row < row_end ? row : row_end - 1;
     a_row[j] = p.A + row * Kc;
-    a_c8[j] = 8 * (u & 7);
+    a_c8[j] = 8 * (u % G::kVR);
     a_dst[j] = r * P + a_c8[j];
   }
-  // weights: forward, W row col0 + tid/2, contraction 32 (tid%2) .. +31 of the
-  // step; input gradient, W row (step row) tid/4, output columns col0 +
-  // 32 (tid%4) .. +31.  Invalid pieces read byte 0 of the tensor and get a
-  // zero scale.
-  const int wl = TRANS ? (tid >> 2) : (tid >> 1);
-  const int wq = TRANS ? (tid & 3) : (tid & 1);
-  const int64_t kblocks = K / BK;
+  // weights: thread piece = PW weights of one W row (kUnits packed dwords).
+  // Forward: W row col0 + tid / kTpr, contraction PW (tid % kTpr) .. of the
+  // step.  Input gradient: W row (contraction) of the step tid / kTpr, output
+  // columns col0 + PW (tid % kTpr) ..  Invalid pieces read byte 0 of the
+  // tensor and get a zero scale.
+  constexpr int kTpr = (TRANS ? BN : BK) / G::PW;       // threads per W row of the step
+  static_assert(kTpr * (TRANS ? BK : BN) == G::kThreads, "one piece per thread");
+  const int wl = tid / kTpr;
+  const int wq = tid % kTpr;
+  const int64_t kblocks = K / 64;
   struct Regs {
     u32x4_t a[G::kAVec];
     u32x4_t w0, w1;
@@ -1552,18 +1601,17 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
     int64_t wrow, wcol;
     if constexpr (TRANS) {
       wrow = static_cast<int64_t>(kt) * BK + wl;
-      wcol = col0 + 32 * wq;
-      r.ok = wrow < N && wcol < K;
+      wcol = col0 + G::PW * wq;
     } else {
       wrow = col0 + wl;
-      wcol = static_cast<int64_t>(kt) * BK + 32 * wq;
-      r.ok = wrow < N;
+      wcol = static_cast<int64_t>(kt) * BK + G::PW * wq;
     }
+    r.ok = wrow < N && wcol < K;
     const int64_t grow = wrow_base + (r.ok ? wrow : 0);
     const int64_t e0 = r.ok ? grow * K + wcol : 0;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + e0);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + (BITS == 8 ? e0 : e0 / 2));
     r.w0 = src[0];
-    r.w1 = src[1];
+    if constexpr (G::kUnits == 8) r.w1 = src[1];
     const int64_t b = r.ok ? grow * kblocks + (wcol >> 6) : 0;
     if constexpr (NESTED) {
       r.sc = static_cast<const uint8_t*>(p.w.absmax)[b];
@@ -1573,34 +1621,56 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
       r.s2 = 0;
     }
   };
-  auto store = [&](int buf, const Regs& r) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < G::kAVec; ++j) *reinterpret_cast<u32x4_t*>(a_buf(buf) + a_dst[j]) = r.a[j];
+  // The staging of one step is split into units so that it can run between
+  // the MFMAs of the step before: activation vector j, and weight unit d
+  // (packed dword d of the piece: 8 NF4 weights or 4 8-bit weights).
+  auto store_a = [&](int buf, const Regs& r, int j) __attribute__((always_inline)) {
+    u32x4_t v = r.a[j];
+    if constexpr (BITS == 4 && !TRANS)    // the contraction order of expand8_eo
+      v = u32x4_t{perm(v[1], v[0], 0x05040100u), perm(v[3], v[2], 0x05040100u),
+                  perm(v[1], v[0], 0x07060302u), perm(v[3], v[2], 0x07060302u)};
+    *reinterpret_cast<u32x4_t*>(a_buf(buf) + a_dst[j]) = v;
+  };
+  auto wscale = [&](const Regs& r) __attribute__((always_inline)) {
     float a;
     if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[r.sc & 0xFF], __uint_as_float(r.s2)), off);
     else a = __uint_as_float(r.sc);
-    a = r.ok ? a : 0.f;
-    uint32_t o[16];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t wd = d < 4 ? r.w0[d] : r.w1[d - 4];
-      const float v0 = __fmul_rn(scode[wd & 0xFFu], a), v1 = __fmul_rn(scode[(wd >> 8) & 0xFFu], a);
-      const float v2 = __fmul_rn(scode[(wd >> 16) & 0xFFu], a), v3 = __fmul_rn(scode[wd >> 24], a);
-      o[2 * d] = pack_bf16x2(v0, v1);
-      o[2 * d + 1] = pack_bf16x2(v2, v3);
-    }
+    return r.ok ? a : 0.f;
+  };
+  auto store_w = [&](int buf, const Regs& r, const Lut& lt, float a, int d) __attribute__((always_inline)) {
     uint16_t* bb = b_buf(buf);
-    if constexpr (TRANS) {
-      // element i of the piece is W_hat[row wl, column 32 wq + i]: output row 32 wq + i
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        bb[(32 * wq + i) * P + wl] = static_cast<uint16_t>(o[i >> 1] >> (16 * (i & 1)));
+    const uint32_t wd = d < 4 ? r.w0[d] : r.w1[d - 4];
+    if constexpr (BITS == 8) {
+      const uint32_t o0 = pack_bf16x2(__fmul_rn(scode[wd & 0xFFu], a), __fmul_rn(scode[(wd >> 8) & 0xFFu], a));
+      const uint32_t o1 = pack_bf16x2(__fmul_rn(scode[(wd >> 16) & 0xFFu], a), __fmul_rn(scode[wd >> 24], a));
+      if constexpr (TRANS) {
+        // element 4 d + e of the piece is W_hat[row wl, column 32 wq + 4 d + e]
+        const int c = 32 * wq + 4 * d;
+        bb[(c + 0) * P + wl] = static_cast<uint16_t>(o0);
+        bb[(c + 1) * P + wl] = static_cast<uint16_t>(o0 >> 16);
+        bb[(c + 2) * P + wl] = static_cast<uint16_t>(o1);
+        bb[(c + 3) * P + wl] = static_cast<uint16_t>(o1 >> 16);
+      } else {
+        *reinterpret_cast<u32x2_t*>(bb + wl * P + 32 * wq + 4 * d) = u32x2_t{o0, o1};
+      }
     } else {
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        *reinterpret_cast<u32x4_t*>(bb + wl * P + 32 * wq + 8 * d) =
-            u32x4_t{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]};
+      uint32_t o[4];
+      expand8_eo(wd, lt, o);
+      uint16_t* dst = TRANS ? bb + wl * PT + G::PW * wq : bb + wl * P + G::PW * wq;
+      *reinterpret_cast<u32x4_t*>(dst + 8 * d) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
+  };
+  auto make_table = [&](float a) __attribute__((always_inline)) {
+    if constexpr (BITS == 4) return make_lut(code, a);
+    else return Lut{};
+  };
+  auto store = [&](int buf, const Regs& r) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < G::kAVec; ++j) store_a(buf, r, j);
+    const float a = wscale(r);
+    const Lut lt = make_table(a);
+#pragma unroll
+    for (int d = 0; d < G::kUnits; ++d) store_w(buf, r, lt, a, d);
   };
 
   // ---- MFMA part ------------------------------------------------------------------
@@ -1613,44 +1683,126 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
     for (int j = 0; j < G::NI; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  auto compute = [&](int buf) __attribute__((always_inline)) {
+  // transposed-read lane offset: rows 8 (g >> 1) + (s >> 2) (+ 4), columns
+  // 16 (g & 1) + 4 (s & 3) of each 32-column fragment (g = lane / 16, s = lane % 16)
+  const int tr_off = (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * PT + wn * G::WN +
+                     16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // a wave whose rows all lie past the tile's last row skips its MFMAs
+  const bool active = row0 + wm * G::WM < row_end;
+  struct Frags {
+    bf16x8_t a[G::MI], b[G::NI];
+  };
+  auto read_frags = [&](int buf, int kk, Frags& f) __attribute__((always_inline)) {
     const uint16_t* ab = a_buf(buf) + (wm * G::WM + r32) * P + 8 * h;
     const uint16_t* bb = b_buf(buf) + (wn * G::WN + r32) * P + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t fa[G::MI], fb[G::NI];
+    for (int i = 0; i < G::MI; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(ab + 32 * i * P + 16 * kk);
 #pragma unroll
-      for (int i = 0; i < G::MI; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(ab + 32 * i * P + 16 * kk);
-#pragma unroll
-      for (int j = 0; j < G::NI; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(bb + 32 * j * P + 16 * kk);
-#pragma unroll
-      for (int i = 0; i < G::MI; ++i)
-#pragma unroll
-        for (int j = 0; j < G::NI; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < G::NI; ++j) {
+      if constexpr (TR) {
+        const uint16_t* src = b_buf(buf) + tr_off + 16 * kk * PT + 32 * j;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * PT));
+        const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
+        f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
+      } else {
+        f.b[j] = *reinterpret_cast<const bf16x8_t*>(bb + 32 * j * P + 16 * kk);
+      }
     }
+  };
+  constexpr int KK = BK / 16;                          // 16-deep MFMA slices per step
+  // One step: the MFMAs of buffer `buf` (fragments read one slice ahead;
+  // none for a wave with no rows in the tile), and, between them, the staging
+  // of the next step's registers `rn` into the other buffer: slice kk stages
+  // weight units 8 kk / KK .. and the activation vectors j with
+  // j KK / kAVec == kk.  ACT and STAGE are compile-time, so each slice is one
+  // basic block the scheduler can interleave.
+  auto step = [&](auto act_c, auto stage_c, int buf, const Regs& rn) __attribute__((always_inline)) {
+    constexpr bool ACT = decltype(act_c)::value, STAGE = decltype(stage_c)::value;
+    float a = 0.f;
+    Lut lt{};
+    if constexpr (STAGE) {
+      a = wscale(rn);
+      lt = make_table(a);
+    }
+    Frags f0, f1;
+    if constexpr (ACT) read_frags(buf, 0, f0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      Frags& fc = (kk & 1) ? f1 : f0;
+      Frags& fn = (kk & 1) ? f0 : f1;
+      if constexpr (ACT) {
+        if (kk + 1 < KK) read_frags(buf, kk + 1, fn);
+#pragma unroll
+        for (int i = 0; i < G::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < G::NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.a[i], fc.b[j], acc[i][j], 0, 0, 0);
+      }
+      if constexpr (STAGE) {
+#pragma unroll
+        for (int d = G::kUnits * kk / KK; d < G::kUnits * (kk + 1) / KK; ++d) store_w(buf ^ 1, rn, lt, a, d);
+#pragma unroll
+        for (int j = 0; j < G::kAVec; ++j)
+          if (j * KK / G::kAVec == kk) store_a(buf ^ 1, rn, j);
+      }
+    }
+  };
+
+  // Registers hold D = kDepth steps: step i multiplies buffer i % 2 and
+  // stages step i + 1 (loaded during step i + 1 - D) into the other buffer,
+  // after the loads of step i + D were issued into the registers step i came
+  // from (staged during step i - 1).  The loop is unrolled by 4 so that the
+  // register set and the buffer of every step are compile-time.
+  constexpr int D = G::kDepth;
+  static_assert(D == 2 || D == 4, "ring of 2 or 4 register sets, unrolled by 4");
+  auto run = [&](auto act_c) __attribute__((always_inline)) {
+    Regs R[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < n) load(j, R[j]);
+    store(0, R[0]);
+    __syncthreads();
+    // step i = i0 + U of the unrolled body (i0 % 4 == 0)
+    auto body = [&](auto u_c, int i) __attribute__((always_inline)) {
+      constexpr int U = decltype(u_c)::value;
+      if (i + D < n) load(i + D, R[U % D]);
+      step(act_c, std::true_type{}, U & 1, R[(U + 1) % D]);
+      __syncthreads();
+    };
+    int i = 0;
+    for (; i + 4 < n; i += 4) {                        // four steps that each stage a next step
+      body(ic<0>{}, i);
+      body(ic<1>{}, i + 1);
+      body(ic<2>{}, i + 2);
+      body(ic<3>{}, i + 3);
+    }
+    // the last 1..4 steps: no loads are left, the final step stages nothing
+    const int rem = n - i;
+    if (rem >= 2) body(ic<0>{}, i);
+    if (rem >= 3) body(ic<1>{}, i + 1);
+    if (rem >= 4) body(ic<2>{}, i + 2);
+    if (rem == 1) step(act_c, std::false_type{}, 0, R[1 % D]);
+    else if (rem == 2) step(act_c, std::false_type{}, 1, R[2 % D]);
+    else if (rem == 3) step(act_c, std::false_type{}, 0, R[3 % D]);
+    else step(act_c, std::false_type{}, 1, R[0]);
   };
 
   __syncthreads();                                     // tables in LDS
   if (n > 0) {
-    Regs r;
-    load(0, r);
-    store(0, r);
-    __syncthreads();
-    for (int i = 0; i < n; ++i) {
-      if (i + 1 < n) load(i + 1, r);
-      compute(i & 1);
-      if (i + 1 < n) store((i + 1) & 1, r);
-      __syncthreads();
-    }
+    if (active) run(std::true_type{});
+    else run(std::false_type{});
   }
 
   // ---- epilogue -------------------------------------------------------------------
+  if (!active) return;
 #pragma unroll
   for (int i = 0; i < G::MI; ++i) {
 #pragma unroll
     for (int j = 0; j < G::NI; ++j) {
-      const int64_t col = col0 + wn * G::WN + 32 * j + r32;
+      int64_t col = col0 + wn * G::WN + 32 * j + r32;
+      // NF4 input gradient: tile column c holds output column 8 (c / 8) + pi(c % 8)
+      if constexpr (TR) col = (col & ~int64_t{7}) | (((col & 3) << 1) | ((col >> 2) & 1));
       if (col >= Nc) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -1664,6 +1816,47 @@ __global__ __launch_bounds__(256) void k_gemm8(GemmParams p) {
       }
     }
   }
+}
+
+template <int BITS, int BM, int NW, bool TRANS, bool NESTED, bool GROUPED>
+hipError_t launch_gt(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
+  using G = GT<BITS, BM, NW>;
+  auto kern = k_gemmt<BITS, BM, NW, TRANS, NESTED, GROUPED>;
+  constexpr int lds = G::kLds(TRANS);
+  static const bool attr_done = [&] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)attr_done;
+  GemmParams q = p;
+  q.m_tiles = static_cast<int32_t>(m_tiles);
+  const int64_t tiles = ((n_cols + G::BN - 1) / G::BN) * m_tiles * p.splits;
+  if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kern<<<dim3(static_cast<unsigned>(tiles)), G::kThreads, lds, stream>>>(q);
+  return hipGetLastError();
+}
+
+// Register-staged tiles: BM = 32, 64 or 128 (8-bit: 32 or 128); NF4 with 4
+// waves, or 8 waves at 64 and 128 rows.
+template <int BITS, bool TRANS, bool GROUPED>
+hipError_t dispatch_gt(int bm, int nw, const GemmParams& p, int64_t m_tiles, int64_t n_cols,
+                       hipStream_t stream) {
+  const bool nested = p.w.nested();
+#define NF4_GT(BMV, NWV)                                                                           \
+  if (bm == BMV && nw == NWV)                                                                      \
+    return nested ? launch_gt<BITS, BMV, NWV, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)    \
+                  : launch_gt<BITS, BMV, NWV, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
+  NF4_GT(32, 4)
+  NF4_GT(128, 4)
+  if constexpr (BITS == 4) {
+    NF4_GT(64, 4)
+    NF4_GT(64, 8)
+    NF4_GT(128, 8)
+  }
+#undef NF4_GT
+  return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, bool TRANS, bool NESTED, bool GROUPED, int C>
@@ -1733,6 +1926,10 @@ hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_t
   if (bm == BMV && bn == BNV && c == CV) {                                                           \
     return nested ? launch_tiled<BMV, BNV, TRANS, true, GROUPED, CV>(p, m_tiles, n_cols, stream)     \
                   : launch_tiled<BMV, BNV, TRANS, false, GROUPED, CV>(p, m_tiles, n_cols, stream);   \
+  }
+  if (c == kStagedTile || c == kStagedTile8) {
+    if (bn != 128) return hipErrorInvalidValue;
+    return dispatch_gt<4, TRANS, GROUPED>(bm, c == kStagedTile8 ? 8 : 4, p, m_tiles, n_cols, stream);
   }
   if (bm == 256 && bn == 256 && c == 0) {
     return nested ? launch_pp<TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
@@ -1804,7 +2001,14 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // compute units (Qwen k/v at M = 2048: 160 tiles, 43 vs 57 us with
   // 128 x 128; the M = 512 q/o input gradients, 32 tiles, stay at 128 x 128).
   const int64_t tiles256 = ((M + 255) / 256) * ((nc + 255) / 256);
-  if ((macs >= 2e10 || (macs >= 4e9 && (kind == GemmKind::kFwd || 2 * tiles256 >= cus))) && M > 128) {
+  // Mid-size products at moderate M take the 8-wave register-staged tiles
+  // (128 x 128, split by the model below): Llama q/o at M = 512, 36.5 us
+  // against 39-40 us with 256-row tiles in either direction (k/v and the
+  // larger gate/down keep the kernels below).
+  const bool staged_mid = M >= 256 && M <= 1024 && macs >= 6e9 && macs < 1.6e10;
+  if (staged_mid) {
+    pl.bm = 128; pl.bn = 128;
+  } else if ((macs >= 2e10 || (macs >= 4e9 && (kind == GemmKind::kFwd || 2 * tiles256 >= cus))) && M > 128) {
     pl.bm = 256; pl.bn = 256;
   } else if (macs >= 4e9 && M > 64) {
     pl.bm = 128; pl.bn = 128;
@@ -1825,7 +2029,16 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // the ping-pong kernel for the forward too
   pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
   if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
-  const int bk = (pl.consumers == 3) ? 64 : 16384 / pl.bn;
+  if (staged_mid && o_bm == 0 && o_bn == 0 && o_c == 0) pl.consumers = kStagedTile8;
+  // NF4_CONSUMERS=5: the register-staged tile kernel, 128 columns, NF4_BM
+  // rows (32, 64 or 128; default 128)
+  if (o_c == kStagedTile || o_c == kStagedTile8) {
+    pl.consumers = o_c;
+    pl.bn = 128;
+    pl.bm = (o_bm == 64 || (o_bm == 32 && o_c == kStagedTile)) ? o_bm : 128;
+  }
+  const bool staged = pl.consumers == kStagedTile || pl.consumers == kStagedTile8;
+  const int bk = (pl.consumers == 3) ? 64 : (staged ? 128 : 16384 / pl.bn);
   const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + pl.bn - 1) / pl.bn);
   const int64_t ksteps = (kc + bk - 1) / bk;
   // Split count: minimise (rounds of workgroups over the compute units) x
@@ -1888,26 +2101,19 @@ GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int3
   pl.bn = 256;
   // rows per expert are only known on the device; size the tile by the mean
   const int64_t mean = (E > 0) ? (total_M + E - 1) / E : total_M;
-  pl.bm = (mean <= 96) ? 64 : (mean <= 192 ? 128 : 256);
-  pl.consumers = (pl.bm == 256) ? 0 : 1;
-  if (mean <= 96) {
-    // Few rows per expert.  A 256-row tile leaves most of its rows empty, but
-    // it expands each weight tile once per expert (a 64-row tile expands it
-    // twice for the experts just over 64 rows) and the 256-row kernels run
-    // faster per step.  Measured on MI355X with 64 experts of 46-86 rows
-    // (OLMoE shapes): the register-operand forward at 256 x 128 for N = 1024
-    // and 256 x 256 for N = 2048 (-3..6% and -22% against 64 x 256); the
-    // ping-pong input gradient for 2048 output columns (-5%), while 64 x 256
-    // stays best for 1024.
-    if (kind == GemmKind::kFwd) {
-      pl.bm = 256;
-      pl.bn = (N >= 2048) ? 256 : 128;
-      pl.consumers = 3;
-    } else if (K >= 2048) {
-      pl.bm = 256;
-      pl.bn = 256;
-      pl.consumers = 0;
-    }
+  if (mean <= 128) {
+    // Few rows per expert: the 8-wave register-staged 128 x 128 tile, one row
+    // tile per expert of up to 128 rows, each weight expanded once per
+    // expert.  Measured on MI355X with 64 experts of 46-86 rows (OLMoE
+    // shapes): gate/up 63 / 79 us forward / input gradient, down 72 / 66 us,
+    // against 98 / 100 and 76 / 95 us with 256-row register-operand and
+    // ping-pong tiles.
+    pl.bm = 128;
+    pl.bn = 128;
+    pl.consumers = kStagedTile8;
+  } else {
+    pl.bm = mean <= 192 ? 128 : 256;
+    pl.consumers = (pl.bm == 256) ? 0 : 1;
   }
   // Tuning overrides (documented): NF4_BM, NF4_BN, NF4_CONSUMERS select the
   // tile as for a single product; there is no split of the contraction here.
@@ -1918,6 +2124,11 @@ GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int3
     if (pl.bm == 256 && !(kind == GemmKind::kFwd && o_bn == 128 && o_c != 2 && o_c != 4)) pl.bn = 256;
     pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
     if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
+    if (o_c == kStagedTile || o_c == kStagedTile8) {
+      pl.consumers = o_c;
+      pl.bn = 128;
+      pl.bm = (o_bm == 64 || (o_bm == 32 && o_c == kStagedTile)) ? o_bm : 128;
+    }
   }
   return pl;
 }
@@ -1994,38 +2205,6 @@ hipError_t launch_grouped(GemmKind kind, const GemmPlan& plan, const void* A,
 
 // ---- 8-bit blockwise matmuls ------------------------------------------------------
 namespace nf4 {
-namespace {
-
-template <int BM, bool TRANS, bool NESTED, bool GROUPED>
-hipError_t launch_g8_t(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
-  auto kern = k_gemm8<BM, TRANS, NESTED, GROUPED>;
-  static const bool attr_done = [&] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, G8<BM>::kLds);
-    (void)hipGetLastError();
-    return true;
-  }();
-  (void)attr_done;
-  GemmParams q = p;
-  q.m_tiles = static_cast<int32_t>(m_tiles);
-  const int64_t tiles = ((n_cols + G8<BM>::BN - 1) / G8<BM>::BN) * m_tiles * p.splits;
-  if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  kern<<<dim3(static_cast<unsigned>(tiles)), 256, G8<BM>::kLds, stream>>>(q);
-  return hipGetLastError();
-}
-
-template <bool TRANS, bool GROUPED>
-hipError_t dispatch_g8(int bm, const GemmParams& p, int64_t m_tiles, int64_t n_cols,
-                       hipStream_t stream) {
-  const bool nested = p.w.nested();
-  if (bm == 32)
-    return nested ? launch_g8_t<32, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
-                  : launch_g8_t<32, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
-  return nested ? launch_g8_t<128, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
-                : launch_g8_t<128, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
-}
-
-}  // namespace
 
 // 128-row tiles, or 32 at M <= 32; the contraction is split (powers of two up
 // to 16) while the tiles alone leave compute units idle and every split keeps
@@ -2062,8 +2241,8 @@ hipError_t launch_gemm8(GemmKind kind, const GemmPlan& plan, const void* A, int6
   p.E = 1;
   p.splits = plan.splits;
   const int64_t m_tiles = (M + plan.bm - 1) / plan.bm;
-  hipError_t e = trans ? dispatch_g8<true, false>(plan.bm, p, m_tiles, nc, stream)
-                       : dispatch_g8<false, false>(plan.bm, p, m_tiles, nc, stream);
+  hipError_t e = trans ? dispatch_gt<8, true, false>(plan.bm, 4, p, m_tiles, nc, stream)
+                       : dispatch_gt<8, false, false>(plan.bm, 4, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 9 : 8);
   if (plan.splits > 1) {
@@ -2095,8 +2274,8 @@ hipError_t launch_grouped8(GemmKind kind, const void* A, const int32_t* offsets,
   p.E = E;
   p.splits = 1;
   const int64_t m_tiles = (total_M + bm - 1) / bm + E;
-  hipError_t e = trans ? dispatch_g8<true, true>(bm, p, m_tiles, nc, stream)
-                       : dispatch_g8<false, true>(bm, p, m_tiles, nc, stream);
+  hipError_t e = trans ? dispatch_gt<8, true, true>(bm, 4, p, m_tiles, nc, stream)
+                       : dispatch_gt<8, false, true>(bm, 4, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 9 : 8);
   return hipSuccess;

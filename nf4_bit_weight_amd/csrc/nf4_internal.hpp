@@ -40,12 +40,17 @@ struct GemmPlan {
   int bm;          // rows of the activation tile
   int bn;          // output columns per tile (256 or 128)
   int consumers;   // MFMA waves per SIMD (1 or 2) beside one expanding wave;
-                   // 0 = the 256 x 256 ping-pong kernel
+                   // 0 = the 256 x 256 ping-pong kernel, 3 = the
+                   // register-operand forward, kStagedTile = the
+                   // register-staged tile kernel (bn = 128, bm = 32/64/128),
+                   // kStagedTile8 the same with 8 waves (bm = 64/128)
   int splits;      // contraction split count (1 = none)
   bool small_m;    // weight-streaming forward (bm = MFMA rows 16 / 32)
   int kc;          // weight-streaming forward: contraction per split
   size_t ws_bytes; // fp32 partials when splits > 1
 };
+constexpr int kStagedTile = 5;    // 4 waves
+constexpr int kStagedTile8 = 6;   // 8 waves (NF4, 64 or 128 rows)
 int device_cu_count();
 GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int32_t E);

@@ -108,13 +108,16 @@ def test_olmoe_experts(proj):
 
 
 @pytest.mark.parametrize("bm,bn,consumers", [(64, 256, 1), (64, 128, 1), (128, 256, 1), (128, 256, 2),
-                                             (128, 128, 1), (256, 256, 4), (256, 256, 0), (256, 128, 0)])
+                                             (128, 128, 1), (256, 256, 4), (256, 256, 0), (256, 128, 0),
+                                             (128, 128, 5), (64, 128, 5), (32, 128, 5),
+                                             (128, 128, 6), (64, 128, 6)])
 def test_grouped_tiles(bm, bn, consumers):
     """Every tile the grouped products can be given through NF4_BM / NF4_BN /
     NF4_CONSUMERS, on ragged experts (empty ones, one spanning two 128-row
     tiles): 256 x 256 is the ping-pong kernel in both directions with
     consumers 4 and the register-operand forward with 0, 256 x 128 the
-    4-wave register-operand forward."""
+    4-wave register-operand forward, consumers 5 / 6 the register-staged tile
+    kernel with 4 / 8 waves."""
     E, N, K = 6, 136, 192
     counts = np.array([3, 0, 70, 129, 0, 1])
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -147,4 +150,43 @@ def test_grouped_tiles(bm, bn, consumers):
     assert_close(y, O.grouped_matmul_fwd(xb, offsets, wb), "grouped y",
                  O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
     assert_close(gx, O.grouped_matmul_bwd_input(gyb, offsets, wb), "grouped grad_x",
+                 O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)
+
+
+@pytest.mark.parametrize("bm,bn,consumers", [(0, 0, 0), (64, 128, 1), (256, 256, 4), (256, 128, 0),
+                                             (128, 128, 5), (128, 128, 6)])
+def test_grouped_many_experts(bm, bn, consumers):
+    """150 experts (three rounds of the 64-lane expert search), many of them
+    empty, several spanning two or three row tiles: every row lands in its
+    expert's slice, forward and input gradient, for the default plan and each
+    kernel family."""
+    E, N, K = 150, 64, 128
+    g = np.random.default_rng(150)
+    counts = g.integers(0, 12, size=E)
+    counts[g.choice(E, 40, replace=False)] = 0
+    counts[[3, 70, 140]] = [140, 300, 129]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(offsets[-1])
+    wq, wb = _stack(E, N, K, True, 15)
+    x = WL.x_bf16(T, K, WL.W_OLMOE, 150)
+    gy = WL.grad_y_bf16(T, N, WL.W_OLMOE, 151)
+    off = torch.from_numpy(offsets).to(DEV)
+    keys = ("NF4_BM", "NF4_BN", "NF4_CONSUMERS")
+    saved = {k: os.environ.get(k) for k in keys}
+    if consumers or bm:
+        os.environ.update({"NF4_BM": str(bm), "NF4_BN": str(bn), "NF4_CONSUMERS": str(consumers)})
+    try:
+        y = api.nf4_grouped_matmul_fwd(x.to(DEV), off, wq, E)
+        gx = api.nf4_grouped_matmul_bwd_input(gy.to(DEV), off, wq, E)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    xb, gyb, aw = WL.bf16_bits(x), WL.bf16_bits(gy), abs_bits(wb)
+    assert_close(y, O.grouped_matmul_fwd(xb, offsets, wb), "150 experts y",
+                 O.grouped_matmul_fwd(abs_bits(xb), offsets, aw), K)
+    assert_close(gx, O.grouped_matmul_bwd_input(gyb, offsets, wb), "150 experts grad_x",
                  O.grouped_matmul_bwd_input(abs_bits(gyb), offsets, aw), N)

@@ -20,9 +20,11 @@ pytestmark = pytest.mark.gpu
 # forward, ping-pong input gradient), 4 = ping-pong for both, 2 = producer /
 # consumer kernel; 256 x 128 is the 4-wave register-operand forward (the input
 # gradient falls back to 256 x 256).  Smaller tiles: MFMA waves per SIMD beside
-# the expanding wave.
+# the expanding wave; 5 = the register-staged tile kernel (128 columns, 128,
+# 64 or 32 rows), 6 = the same with 8 waves (128 or 64 rows).
 TILES = [(256, 256, 0), (256, 128, 0), (256, 256, 4), (256, 256, 2), (128, 256, 1), (128, 256, 2),
-         (64, 256, 1), (128, 128, 1), (64, 128, 1)]
+         (64, 256, 1), (128, 128, 1), (64, 128, 1), (128, 128, 5), (64, 128, 5), (32, 128, 5),
+         (128, 128, 6), (64, 128, 6)]
 
 
 @pytest.fixture
@@ -125,10 +127,13 @@ RING_TILES = [(256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1), (128, 1
 # only): its weight copies run three steps ahead through three slots, and the
 # last steps issue no copies, so its short contractions need the same sweep.
 PP_TILES = [(256, 256, 4), (256, 256, 0)]
+# The register-staged tile kernel (4 or 8 waves): 128-deep steps, the next step's operands
+# held in registers, two LDS buffers.
+STAGED_TILES = [(128, 128, 5), (64, 128, 5), (32, 128, 5), (128, 128, 6), (64, 128, 6)]
 
 
 @pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 10, 11, 13])
-@pytest.mark.parametrize("bm,bn,consumers", RING_TILES + PP_TILES)
+@pytest.mark.parametrize("bm,bn,consumers", RING_TILES + PP_TILES + STAGED_TILES)
 def test_tiled_step_counts(steps, bm, bn, consumers, plan_override):
     """One workgroup's contraction of 1 to 13 steps in both directions: every
     remainder of the unrolled step loop with and without a whole period, and
