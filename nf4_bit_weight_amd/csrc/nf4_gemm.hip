@@ -1532,9 +1532,21 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
   const int64_t Kc = TRANS ? N : K;
   const int ktiles = static_cast<int>((Kc + BK - 1) / BK);
 
-  const int tt = xcd_tile(blockIdx.x, gridDim.x);
-  const int mt = tt % p.m_tiles;
-  const int cz = tt / p.m_tiles;
+  int mt, cz;
+  if constexpr (GROUPED) {
+    // An expert's weight tiles serve only its own rows, while its activation
+    // rows are shared by all of its column tiles: XCD x (workgroups are
+    // dealt to the 8 XCDs in turn) serves row tiles x, x + 8, ..., each
+    // with all its column tiles in a row, so those activations are fetched
+    // into one L2.  m_tiles is a multiple of 8 here and splits = 1.
+    const int idx = static_cast<int>(blockIdx.x >> 3), nct = static_cast<int>(gridDim.x) / p.m_tiles;
+    mt = 8 * (idx / nct) + static_cast<int>(blockIdx.x & 7);
+    cz = idx % nct;
+  } else {
+    const int tt = xcd_tile(blockIdx.x, gridDim.x);
+    mt = tt % p.m_tiles;
+    cz = tt / p.m_tiles;
+  }
   const int z = cz % p.splits;
   const int64_t col0 = static_cast<int64_t>(cz / p.splits) * BN;
   int64_t row0, row_end, wrow_base;
@@ -1711,7 +1723,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
     }
   };
   constexpr int KK = BK / 16;                          // 16-deep MFMA slices per step
-  // One step: the MFMAs of buffer `buf` (fragments read one slice ahead;
+  // One step: the MFMAs of buffer `buf` (fragments read two slices ahead;
   // none for a wave with no rows in the tile), and, between them, the staging
   // of the next step's registers `rn` into the other buffer: slice kk stages
   // weight units 8 kk / KK .. and the activation vectors j with
@@ -1725,14 +1737,19 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
       a = wscale(rn);
       lt = make_table(a);
     }
-    Frags f0, f1;
-    if constexpr (ACT) read_frags(buf, 0, f0);
+    // fragments are read two slices ahead (a ring of three): with two MFMAs
+    // per slice and wave (8 waves), one slice ahead left the reads' LDS
+    // latency in front of every MFMA pair
+    Frags f[3];
+    if constexpr (ACT) {
+      read_frags(buf, 0, f[0]);
+      if (KK > 1) read_frags(buf, 1, f[1]);
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      Frags& fc = (kk & 1) ? f1 : f0;
-      Frags& fn = (kk & 1) ? f0 : f1;
       if constexpr (ACT) {
-        if (kk + 1 < KK) read_frags(buf, kk + 1, fn);
+        if (kk + 2 < KK) read_frags(buf, kk + 2, f[(kk + 2) % 3]);
+        const Frags& fc = f[kk % 3];
 #pragma unroll
         for (int i = 0; i < G::MI; ++i)
 #pragma unroll
@@ -1746,6 +1763,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
         for (int j = 0; j < G::kAVec; ++j)
           if (j * KK / G::kAVec == kk) store_a(buf ^ 1, rn, j);
       }
+      // keep each slice's reads, MFMAs and staging together: without the
+      // fence the scheduler moves MFMAs up next to their own reads
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -1831,6 +1851,9 @@ hipError_t launch_gt(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipSt
   }();
   (void)attr_done;
   GemmParams q = p;
+  // grouped: row tiles dealt to the XCDs in turn (a multiple of 8; the
+  // extra ids past the real tiles exit at once)
+  if constexpr (GROUPED) m_tiles = (m_tiles + 7) / 8 * 8;
   q.m_tiles = static_cast<int32_t>(m_tiles);
   const int64_t tiles = ((n_cols + G::BN - 1) / G::BN) * m_tiles * p.splits;
   if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;

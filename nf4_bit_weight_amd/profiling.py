@@ -43,8 +43,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/nf4_gemm.hip", "csrc/nf4_gemv.hip", "csrc/nf4_device.hpp")
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
-FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_gemv_ln<", "k_gemm8<", "k_splitk_reduce")
-MFMA_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_gemv_ln<", "k_gemm8<")
+FUSED_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_gemv_ln<", "k_gemmt<", "k_splitk_reduce")
+MFMA_KERNELS = ("k_gemm<", "k_pp<", "k_rb<", "k_gemv<", "k_gemv_ln<", "k_gemmt<")
 
 
 def _code_only(text: str) -> str:
