@@ -1,7 +1,6 @@
-"""Copy waits of the two kernels that count their own copies, checked on the
-host against their issue order (the ping-pong input gradient waits for all of
-its copies every step, and the streaming kernel leaves its waits to the
-compiler).
+"""Copy waits of the kernels that count their own copies, checked on the host
+against their issue order: the producer/consumer tiles, the register-operand
+forward and the ping-pong tiles.
 
 The producer waves of the (BM x BN) tiled kernel issue LDS-direct copies that
 complete in issue order and wait on them with vmcnt(c), i.e. until at most c of
@@ -161,3 +160,77 @@ def test_register_operand_replay_catches_a_short_wait():
     ex["step_a"] = "kCopies + kWCopies + 1"
     with pytest.raises(AssertionError, match="activation tile"):
         _replay_rb(2, 3, 4, ex)
+
+
+# ---- the ping-pong kernel ----------------------------------------------------------
+# Per wave: a prologue A(0) (four copy groups), W(0), W(1), W(2) (kWc copies
+# each: the packed bytes, plus a scale on waves 0-3 or a nested scale on
+# waves 4-7 of the nested form), then a wait that leaves only W(2) in flight.
+# Step i issues A(i + 1) (if there is a step i + 1) and then W(i + 3) (if
+# there is a step i + 3) and ends with a wait that leaves only the newest
+# weight copies in flight.  Step i reads A(i) and the weights of step i + 1.
+
+def _pp_exprs():
+    s = open(SRC).read()
+    body = s[s.index("void k_pp(GemmParams p)"):s.index("void k_rb(")]
+    end = re.search(r"auto end_step = .*?if \(i \+ (\d) < n\) \{\s*if \(two_w\) wait_vm\(ic<(\d)>\{\}\);"
+                    r"\s*else wait_vm\(ic<(\d)>\{\}\);\s*\} else \{\s*wait_vm\(ic<(\d)>\{\}\);", body, re.S)
+    dma = re.search(r"if \(g == 3 && ci \+ (\d) < n\) \{\s*issue_wpk\(ci \+ (\d), ci % (\d)\);", body)
+    pro = re.search(r"if \(n > 2\) \{\s*issue_wpk\(2, 2\);\s*issue_ws\(2, 2\);\s*if \(two_w\) wait_vm\(ic<(\d)>\{\}\);"
+                    r"[^\n]*\n\s*else wait_vm\(ic<(\d)>\{\}\);\s*\} else \{\s*wait_vm\(ic<(\d)>\{\}\);", body, re.S)
+    assert end and dma and pro, "ping-pong copy and wait code not found"
+    assert end.group(1) == dma.group(1) == dma.group(2), "weights issued and waited at the same distance"
+    return {"ahead": int(dma.group(1)), "slots": int(dma.group(3)),
+            "end": {2: int(end.group(2)), 1: int(end.group(3)), "last": int(end.group(4))},
+            "pro": {2: int(pro.group(1)), 1: int(pro.group(2)), "short": int(pro.group(3))}}
+
+
+def _replay_pp(kA, kWc, n, ex):
+    ops, done = [], 0
+
+    def issue(kind, step, count):
+        ops.extend([(kind, step)] * count)
+
+    def wait(c):
+        nonlocal done
+        done = max(done, len(ops) - c)
+
+    def landed(kind, step):
+        return max(k for k, o in enumerate(ops) if o == (kind, step)) < done
+
+    D = ex["ahead"]
+    issue("A", 0, 4 * kA)
+    for j in range(min(n, D)):
+        issue("W", j, kWc)
+    wait(ex["pro"][kWc] if n > 2 else ex["pro"]["short"])
+    assert landed("A", 0) and landed("W", 0), "prologue: step 0"
+    if n > 1:
+        assert landed("W", 1), "prologue: weights of step 1, expanded in step 0"
+    for i in range(n):
+        if i + 1 < n:
+            issue("A", i + 1, 4 * kA)
+        if i + D < n:
+            issue("W", i + D, kWc)
+        wait(ex["end"][kWc] if i + D < n else ex["end"]["last"])
+        if i + 1 < n:
+            assert landed("A", i + 1), f"end of step {i}: activation tile of step {i + 1}"
+        if i + 2 < n:
+            assert landed("W", i + 2), f"end of step {i}: weights of step {i + 2}"
+    # every slot is refilled only after its step was expanded: W(i + D) goes
+    # into slot i % slots, the slot of step i, expanded during step i - 1
+    assert ex["slots"] == D
+
+
+def test_ping_pong_copy_waits_cover_every_read():
+    ex = _pp_exprs()
+    for kA in (1, 2):
+        for kWc in (1, 2):
+            for n in range(1, 14):
+                _replay_pp(kA, kWc, n, ex)
+
+
+def test_ping_pong_replay_catches_a_short_wait():
+    ex = _pp_exprs()
+    ex["end"] = {**ex["end"], 2: 3}             # one copy more left in flight than the newest weights
+    with pytest.raises(AssertionError, match="end of step"):
+        _replay_pp(1, 2, 6, ex)
