@@ -1,37 +1,35 @@
-// Small-M forward y = x . W_hat^T (M <= 32): weight-streaming kernel.
+// Small-M forward y = x . W_hat^T (M <= 32): weight-streaming kernels.
 //
 // At decode sizes the product is bound by HBM and by the expansion: every
 // packed byte of W is used by at most 32 rows of x (Soup issue #842, "Nuance",
 // on the small-batch regime where a fused 4-bit GEMV is the fast path).  The
-// kernel therefore streams W once, with each lane expanding whole 64-blocks,
-// and keeps x on chip.
+// kernels therefore stream W once, with each lane expanding whole 64-blocks,
+// and keep x on chip.  Two kernels share that plan:
 //
-//   * A workgroup owns RW * MP rows of W and one contraction chunk.  Its
-//     RW * KW waves are arranged as RW row groups of MP rows times KW
-//     contraction slices: the KW waves of a row group split the chunk's steps
-//     between them, and their fp32 results are added through LDS in the fixed
-//     order 0 .. KW-1.  Splitting the contraction inside the workgroup gives
-//     enough waves to cover HBM latency without partial sums in HBM; chunks
-//     across workgroups (summed by the fixed-order split reduction) are only
-//     used when the x chunk would not fit in LDS.
-//   * The MFMA is v_mfma_f32_16x16x32_bf16 (MP = 16) or
-//     v_mfma_f32_32x32x16_bf16 (MP = 32); its A operand is x (rows >= M read
-//     a zero row), its B operand the expanded weights.
+//   * k_gemv_ln (below; up to M = 24, and small products to M = 32): 16-row
+//     W groups, whole 128-byte lines copied global -> LDS per wave.
+//   * k_gemv (large products above M = 24): 32-row W groups, each lane loads
+//     its own block with two 16-byte loads.
+//
+// Common to both:
+//   * A workgroup owns RW row groups of W and one contraction chunk.  Its
+//     RW * KW waves are arranged as RW row groups times KW contraction
+//     slices: the KW waves of a row group split the chunk's steps between
+//     them, and their fp32 results are added through LDS in the fixed order
+//     0 .. KW-1.  Splitting the contraction inside the workgroup gives enough
+//     waves to cover HBM latency without partial sums in HBM; chunks across
+//     workgroups (summed by the fixed-order split reduction) are only used
+//     when the x chunk would not fit in LDS.
+//   * The MFMA's A operand is x (rows >= M read a zero row), its B operand
+//     the expanded weights.
 //   * The contraction is permuted inside each step so that a lane's k-group
-//     is one whole NF4 block: lane (n = l % MP, g = l / MP) of MFMA t reads
-//     k = 64 * (G * s + g) + 8 t .. + 7 of step s (G = 64 / MP blocks).  A
-//     lane builds one 16-entry byte table per block and expands one dword of
-//     its block's 32 packed bytes per MFMA.  At MP = 16 the packed bytes are
-//     fetched as whole 128-byte lines (8 lanes per line) and handed to their
-//     lanes through a per-wave LDS buffer; at MP = 32 each lane loads its own
-//     block with two 16-byte loads.
-//   * Block scales are loaded a batch of PD steps ahead of that batch's
-//     packed bytes and decoded at the batch start.
+//     is one whole NF4 block: lane (n = l % R, g = l / R) of MFMA t reads
+//     k = 64 * (G * s + g) + 8 t .. + 7 of step s (R rows per group, G = 64 / R
+//     blocks per step).  A lane builds one 16-entry byte table per block and
+//     expands one dword of its block's 32 packed bytes per MFMA.
 //   * Within each 8-element group the expansion emits the order
 //     (0, 2, 4, 6, 1, 3, 5, 7), which saves the final interleave; x is staged
 //     into LDS in the same order, so every product pairs the right elements.
-//   * Packed loads run PD steps ahead in registers, and the first PD are in
-//     flight while x is staged.
 #include <stdlib.h>
 
 #include <type_traits>
@@ -45,15 +43,6 @@ namespace {
 constexpr int kPD = 4;                    // packed-weight prefetch distance (steps)
 constexpr int kXBudgetBytes = 64 * 1024;  // LDS for the staged x chunk (M + 1 rows)
 constexpr int kMaxWaves = 16;
-// MP = 16: one step of a wave is 16 W rows x 128 contiguous bytes.  The packed
-// bytes are fetched line by line (lane l: 16-byte piece l % 8 of row l / 8,
-// then of row 8 + l / 8), so every load instruction covers 8 whole 128-byte
-// lines; a wave-private LDS buffer (rows padded to 144 bytes against bank
-// conflicts) hands each lane its own block's 32 bytes.  Measured: fetching a
-// block per lane instead (every line split over two instructions) halves the
-// achieved HBM rate of the weight stream.
-constexpr int kTRowPitch = 144;
-constexpr int kTBufBytes = 16 * kTRowPitch;
 
 struct GemvParams {
   const uint16_t* x;     // [M, K] bf16
@@ -63,29 +52,22 @@ struct GemvParams {
   int32_t M;
   int32_t splits;
   int32_t kc;            // contraction per chunk (multiple of the step)
-  int32_t tb_off;        // byte offset of the per-wave line buffers in dynamic LDS (MP = 16)
+  int32_t tb_off;        // line-staged kernel: byte offset of the per-wave staging slots in dynamic LDS
 };
-
-template <int MP>
-struct Gv {
-  static constexpr int G = 64 / MP;               // blocks per step
-  static constexpr int kStepK = 64 * G;           // 256 or 128
-  static constexpr int kAccRegs = MP == 16 ? 4 : 16;
-};
-
-template <int MP>
-using acc_t = typename std::conditional<MP == 16, f32x4_t, f32x16_t>::type;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-template <int MP, int RW, int KW, bool NESTED, int MH>
+// 32-row groups: one step is 128 columns (two 64-blocks per row), MFMA
+// v_mfma_f32_32x32x16_bf16, 16 accumulator registers per lane.  Packed loads
+// run kPD steps ahead in registers, the first kPD in flight while x is
+// staged; block scales are loaded a batch of kPD steps ahead of that batch's
+// packed bytes and decoded at the batch start.
+template <int RW, int KW, bool NESTED>
 __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
-  using S = Gv<MP>;
-  static_assert(MH == 1 || MP == 16, "two x halves only with 16-row groups");
+  constexpr int MP = 32, kStepK = 128, kAccRegs = 16;
   constexpr int kThr = 64 * RW * KW;
-  constexpr int kRegs = S::kAccRegs * MH;       // accumulator registers per lane
   // [M + 1][kc + 8] bf16 (row M is zero), reused for the cross-wave sums
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ float sncode[256];
@@ -102,7 +84,7 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   const int pitch = kc + 8;                      // elements; rows land on distinct banks
 
   // ---- this wave's steps of the chunk: a contiguous run ------------------------
-  const int nsteps = static_cast<int>((k1 - k0 + S::kStepK - 1) / S::kStepK);
+  const int nsteps = static_cast<int>((k1 - k0 + kStepK - 1) / kStepK);
   const int per = (nsteps + KW - 1) / KW;
   const int s_begin = kw * per < nsteps ? kw * per : nsteps;
   const int s_end = s_begin + per < nsteps ? s_begin + per : nsteps;
@@ -130,13 +112,13 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   // step (an address already read), so every load stays inside the tensor
   auto clamp_step = [&](int ls) { return s_begin + (ls < nw ? ls : (nw > 0 ? nw - 1 : 0)); };
   auto step_valid = [&](int ls) {
-    const int64_t koff = k0 + static_cast<int64_t>(S::kStepK) * clamp_step(ls) + 64 * g;
+    const int64_t koff = k0 + static_cast<int64_t>(kStepK) * clamp_step(ls) + 64 * g;
     return row_ok & (koff < k1) & (nw > 0);
   };
   auto load_scales = [&](int ls0, Scales& sq) {
 #pragma unroll
     for (int j = 0; j < kPD; ++j) {
-      const int64_t koff = k0 + static_cast<int64_t>(S::kStepK) * clamp_step(ls0 + j) + 64 * g;
+      const int64_t koff = k0 + static_cast<int64_t>(kStepK) * clamp_step(ls0 + j) + 64 * g;
       const bool v = row_ok & (koff < k1) & (nw > 0);
       const uint64_t bb = v ? static_cast<uint64_t>(row_base + koff) >> 6 : 0;
       if constexpr (NESTED) {
@@ -148,28 +130,15 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
       }
     }
   };
+  // the lane's block of step ls (blocks past the end, or rows past N, read
+  // the tensor's first bytes; their consumers see a zero scale)
   auto load = [&](int ls, Raw& q) {
-    const int64_t kstep = k0 + static_cast<int64_t>(S::kStepK) * clamp_step(ls);
-    if constexpr (MP == 16) {
-      // whole lines: piece pc of rows lr and 8 + lr of the row group (pieces
-      // of blocks past the end, or rows past N, read the tensor's first bytes;
-      // their consumers see a zero scale)
-      const int lr = lane >> 3, pc = lane & 7;
-      const int64_t nA = (static_cast<int64_t>(blockIdx.x) * RW + rw) * MP + lr;
-      const int64_t kp = kstep + 32 * pc;
-      const bool okk = (kp < k1) & (nw > 0);
-      const uint64_t fa = (okk & (nA < N)) ? static_cast<uint64_t>(nA * K + kp) : 0;
-      const uint64_t fb = (okk & (nA + 8 < N)) ? static_cast<uint64_t>((nA + 8) * K + kp) : 0;
-      q.pk0 = *reinterpret_cast<const u32x4_t*>(p.w.packed + (fa >> 1));
-      q.pk1 = *reinterpret_cast<const u32x4_t*>(p.w.packed + (fb >> 1));
-    } else {
-      const int64_t koff = kstep + 64 * g;
-      const bool v = row_ok & (koff < k1) & (nw > 0);
-      const uint64_t flat = v ? static_cast<uint64_t>(row_base + koff) : 0;   // multiple of 64
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + (flat >> 1));
-      q.pk0 = src[0];
-      q.pk1 = src[1];
-    }
+    const int64_t koff = k0 + static_cast<int64_t>(kStepK) * clamp_step(ls) + 64 * g;
+    const bool v = row_ok & (koff < k1) & (nw > 0);
+    const uint64_t flat = v ? static_cast<uint64_t>(row_base + koff) : 0;   // multiple of 64
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(p.w.packed + (flat >> 1));
+    q.pk0 = src[0];
+    q.pk1 = src[1];
   };
 
   // The fences keep every prefetch where it is written: without them the
@@ -258,18 +227,12 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
   }
   __syncthreads();
 
-  acc_t<MP> acc[MH];
+  f32x16_t acc;
 #pragma unroll
-  for (int h = 0; h < MH; ++h)
-#pragma unroll
-    for (int i = 0; i < S::kAccRegs; ++i) acc[h][i] = 0.f;
+  for (int i = 0; i < kAccRegs; ++i) acc[i] = 0.f;
 
-  // A fragments of MFMA t: x row r, and r + 16 for the second half at M > 16
-  // (rows >= M read the zero row M)
-  const uint16_t* xrow[MH];
-#pragma unroll
-  for (int h = 0; h < MH; ++h) xrow[h] = xs + (r + 16 * h < M ? r + 16 * h : M) * pitch + 64 * g;
-  uint8_t* const tbuf = reinterpret_cast<uint8_t*>(xs) + p.tb_off + wave * kTBufBytes;
+  // A fragments of MFMA t: x row r (rows >= M read the zero row M)
+  const uint16_t* const xrow = xs + (r < M ? r : M) * pitch + 64 * g;
   // decoded scale of each step of the current batch (zero for blocks past the ends)
   float a_dec[kPD];
   auto decode = [&](int ls0, const Scales& sq) {
@@ -282,43 +245,22 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
     }
   };
   auto step = [&](int ls, int j, const Raw& q) {
-    // one x half: all eight A fragments first, so their LDS latency overlaps
-    // the table build; two halves: read at their MFMAs (registers)
-    const int xo = S::kStepK * (s_begin + ls);
+    // all eight A fragments first, so their LDS latency overlaps the table build
+    const int xo = kStepK * (s_begin + ls);
     bf16x8_t afr[8];
-    if constexpr (MH == 1) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) afr[t] = *reinterpret_cast<const bf16x8_t*>(xrow[0] + xo + 8 * t);
-    }
+    for (int t = 0; t < 8; ++t) afr[t] = *reinterpret_cast<const bf16x8_t*>(xrow + xo + 8 * t);
     // the packed registers are redefined at the step's start, so no
     // arithmetic on them is scheduled (and waited for) earlier
     u32x4_t d0 = q.pk0, d1 = q.pk1;
     asm volatile("" : "+v"(d0), "+v"(d1));
-    if constexpr (MP == 16) {
-      // through the wave's line buffer: rows lr and 8 + lr in, block g of row r out
-      const int lr = lane >> 3, pc = lane & 7;
-      *reinterpret_cast<u32x4_t*>(tbuf + lr * kTRowPitch + 16 * pc) = d0;
-      *reinterpret_cast<u32x4_t*>(tbuf + (8 + lr) * kTRowPitch + 16 * pc) = d1;
-      d0 = *reinterpret_cast<const u32x4_t*>(tbuf + r * kTRowPitch + 32 * g);
-      d1 = *reinterpret_cast<const u32x4_t*>(tbuf + r * kTRowPitch + 32 * g + 16);
-    }
     const Lut lt = make_lut(code, a_dec[j]);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       uint32_t o[4];
       expand8_eo(t < 4 ? d0[t] : d1[t - 4], lt, o);
       const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
-      if constexpr (MP == 16 && MH == 1) {
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[t], bfr, acc[0], 0, 0, 0);
-      } else if constexpr (MP == 16) {
-        // the expanded fragment serves both halves of x (fragments read here)
-#pragma unroll
-        for (int h = 0; h < MH; ++h)
-          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              *reinterpret_cast<const bf16x8_t*>(xrow[h] + xo + 8 * t), bfr, acc[h], 0, 0, 0);
-      } else {
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[t], bfr, acc[0], 0, 0, 0);
-      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr[t], bfr, acc, 0, 0, 0);
     }
   };
 
@@ -359,35 +301,27 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
     float* red = reinterpret_cast<float*>(xs);         // [KW-1][RW][regs][64]
     if (kw > 0) {
 #pragma unroll
-      for (int h = 0; h < MH; ++h)
-#pragma unroll
-        for (int i = 0; i < S::kAccRegs; ++i)
-          red[(((kw - 1) * RW + rw) * kRegs + h * S::kAccRegs + i) * 64 + lane] = acc[h][i];
+      for (int i = 0; i < kAccRegs; ++i) red[(((kw - 1) * RW + rw) * kAccRegs + i) * 64 + lane] = acc[i];
     }
     __syncthreads();
     if (kw > 0) return;
     for (int v = 1; v < KW; ++v) {
 #pragma unroll
-      for (int h = 0; h < MH; ++h)
-#pragma unroll
-        for (int i = 0; i < S::kAccRegs; ++i)
-          acc[h][i] = __fadd_rn(acc[h][i], red[(((v - 1) * RW + rw) * kRegs + h * S::kAccRegs + i) * 64 + lane]);
+      for (int i = 0; i < kAccRegs; ++i)
+        acc[i] = __fadd_rn(acc[i], red[(((v - 1) * RW + rw) * kAccRegs + i) * 64 + lane]);
     }
   }
 
   // ---- epilogue: lane holds output column n; rows as laid out by the MFMA ----
   if (!row_ok) return;
 #pragma unroll
-  for (int h = 0; h < MH; ++h) {
-#pragma unroll
-    for (int i = 0; i < S::kAccRegs; ++i) {
-      const int m = MP == 16 ? 16 * h + 4 * (lane / 16) + i : 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
-      if (m >= M) continue;
-      if (p.splits == 1) {
-        p.y[static_cast<int64_t>(m) * N + n] = to_bf16(acc[h][i]);
-      } else {
-        p.partial[(static_cast<int64_t>(z) * M + m) * N + n] = acc[h][i];
-      }
+  for (int i = 0; i < kAccRegs; ++i) {
+    const int m = 8 * (i / 4) + 4 * (lane / 32) + (i % 4);
+    if (m >= M) continue;
+    if (p.splits == 1) {
+      p.y[static_cast<int64_t>(m) * N + n] = to_bf16(acc[i]);
+    } else {
+      p.partial[(static_cast<int64_t>(z) * M + m) * N + n] = acc[i];
     }
   }
 }
@@ -409,16 +343,22 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 // step's block scales (one per lane) arrive the same way, a byte or a dword
 // per lane.  Every load of the loop is such a copy, issued kSD steps ahead;
 // one explicit vmcnt per step is the only wait on memory, and a slot is only
-// refilled by the wave that reads it, so the loop has no barrier.  Two slots
+// refilled by the wave that reads it, so the loop has no barrier.  No two
+// copies in flight read the same bytes: a repeated copy of the same address
+// let a counted wait pass before the older copy had landed (below).  So the
+// nested scales, which consecutive steps share (one per 256 blocks), are not
+// copied per step: a chunk holds at most 64 steps, so a lane's blocks span
+// fewer than 256 and meet at most two nested groups, whose two scales the
+// lane loads into registers once, before its first copy.  Two slots
 // per wave keep a workgroup's LDS small enough that the launches of the
 // decode shapes are resident in one round (measured: four slots halved the
 // resident workgroups and made the forward of gate at M = 1 18 us instead of
-// 15).  The buffer
-// resources carry the tensor bounds (reads past the end return zero) and move
-// with the step in scalar registers: the loop computes no vector addresses
-// except the nested-scale index.
+// 15).  The buffer resources carry the tensor bounds (reads past the end
+// return zero) and move with the step in scalar registers: the loop computes
+// no vector addresses.
 constexpr int kSD = 2;                          // staging slots per wave = copy distance (steps)
-constexpr int kSlotBytes = 2048 + 256 + 256;    // packed lines, block scales, nested scales
+constexpr int kSlotBytes = 2048 + 256;          // packed lines, block scales
+constexpr int kLnMaxChunkSteps = 64;            // chunk length bound the nested-scale pair relies on
 constexpr int kLnMaxWaves = 8;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
 
@@ -436,7 +376,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 template <int RW, int KW, bool NESTED, int MH>
 __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
   constexpr int kThr = 64 * RW * KW;
-  constexpr int C = NESTED ? 4 : 3;             // copy instructions per step
+  constexpr int C = 3;                          // copy instructions per step
   // [M + 1][kc + 8] bf16 (row M is zero), reused for the cross-wave sums;
   // the waves' staging slots follow at byte p.tb_off
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
@@ -486,10 +426,6 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
     if constexpr (NESTED) {
       const auto ra = rsrc(static_cast<const uint8_t*>(p.w.absmax) + bb, nb - bb);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 1, lane_b, 0, 0, 0);
-      const int64_t bh = bb >> 8;
-      const uint32_t vn = ((static_cast<uint32_t>(bb & 255) + lane_b) >> 8) << 2;
-      const auto rn = rsrc(p.w.nested_absmax + bh, 4 * (ng - bh));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rn, (lds_void_t*)(sl + 2304), 4, vn, 0, 0, 0);
     } else {
       const auto ra = rsrc(static_cast<const float*>(p.w.absmax) + bb, 4 * (nb - bb));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, 4u * lane_b, 0, 0, 0);
@@ -552,13 +488,22 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
       }
     }
   };
-  // the nested table (256 entries over the workgroup's threads)
+  // the nested table (256 entries over the workgroup's threads), and the
+  // lane's nested scales: groups g0 (its block of its first step) and g0 + 1
+  // (blocks of its later steps: 4 per step, at most 64 steps, so fewer than
+  // 256 further on); indices clamped into the tensor (rows past N are never
+  // stored, blocks past K meet zero x)
   constexpr int kNC = (256 + kThr - 1) / kThr;
   float nc_reg[kNC];
+  const int64_t blk0 = (rg0 + r) * kb + (k0 >> 6) + 4 * static_cast<int64_t>(s_begin) + g;
+  const int64_t g0 = blk0 >> 8;
+  float s2a = 0.f, s2b = 0.f;
   x_load(0);
   if constexpr (NESTED) {
 #pragma unroll
     for (int j = 0; j < kNC; ++j) nc_reg[j] = tid + j * kThr < 256 ? p.w.ncode[tid + j * kThr] : 0.f;
+    s2a = p.w.nested_absmax[g0 < ng ? g0 : ng - 1];
+    s2b = p.w.nested_absmax[g0 + 1 < ng ? g0 + 1 : ng - 1];
   }
   fence();
   // Only copies that will be read are issued.  (Measured: a wave of one step
@@ -590,7 +535,7 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
   __builtin_amdgcn_s_barrier();
   fence();
 
-  acc_t<16> acc[MH];
+  f32x4_t acc[MH];
 #pragma unroll
   for (int h = 0; h < MH; ++h)
 #pragma unroll
@@ -608,23 +553,22 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
 
   struct Staged {
     u32x4_t lo, hi;
-    uint32_t sc, s2;
+    uint32_t sc;
   };
 #define NF4_LN_READ(OFF)                                                                   \
-  asm volatile("ds_read_b128 %0, %4 offset:" #OFF "\n\t"                                   \
-               "ds_read_b128 %1, %5 offset:" #OFF "\n\t"                                   \
-               "ds_read_b32 %2, %6 offset:" #OFF "\n\t"                                    \
-               "ds_read_b32 %3, %6 offset:" #OFF "+256\n\t"                                \
+  asm volatile("ds_read_b128 %0, %3 offset:" #OFF "\n\t"                                   \
+               "ds_read_b128 %1, %4 offset:" #OFF "\n\t"                                   \
+               "ds_read_b32 %2, %5 offset:" #OFF "\n\t"                                    \
                "s_waitcnt lgkmcnt(0)"                                                      \
-               : "=v"(u.lo), "=v"(u.hi), "=v"(u.sc), "=v"(u.s2)                            \
+               : "=v"(u.lo), "=v"(u.hi), "=v"(u.sc)                                        \
                : "v"(a_lo), "v"(a_hi), "v"(a_sc)                                           \
                : "memory")
   auto read_slot = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    static_assert(kSlotBytes == 2560 && kSD == 2, "slot offsets below");
+    static_assert(kSlotBytes == 2304 && kSD == 2, "slot offsets below");
     Staged u;
     if constexpr (slot == 0) NF4_LN_READ(0);
-    else NF4_LN_READ(2560);
+    else NF4_LN_READ(2304);
     return u;
   };
 #undef NF4_LN_READ
@@ -638,8 +582,12 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
       for (int t = 0; t < 8; ++t) afr[h][t] = *reinterpret_cast<const bf16x8_t*>(xrow[h] + xo + 8 * t);
     const Staged u = read_slot(slot_c);
     float a;
-    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[u.sc & 0xFF], __uint_as_float(u.s2)), off);
-    else a = __uint_as_float(u.sc);
+    if constexpr (NESTED) {
+      const float s2 = ((blk0 + 4 * ls) >> 8) == g0 ? s2a : s2b;
+      a = __fadd_rn(__fmul_rn(sncode[u.sc & 0xFF], s2), off);
+    } else {
+      a = __uint_as_float(u.sc);
+    }
     const Lut lt = make_lut(code, a);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -717,24 +665,20 @@ size_t gemv_region_bytes(int mp, int rw, int kw, int64_t M, int kc) {
   const size_t rb = static_cast<size_t>(kw - 1) * rw * regs * 64 * 4;
   return ((xb > rb ? xb : rb) + 15) / 16 * 16;
 }
-// plus the per-wave line buffers (MP = 16)
-size_t gemv_lds_bytes(int mp, int rw, int kw, int64_t M, int kc) {
-  return gemv_region_bytes(mp, rw, kw, M, kc) + (mp == 16 ? static_cast<size_t>(rw) * kw * kTBufBytes : 0);
-}
+constexpr size_t kGemvLdsMax = kXBudgetBytes + 4096;
 
-template <int MP, int RW, int KW, bool NESTED, int MH>
+template <int RW, int KW, bool NESTED>
 hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
-  auto kern = k_gemv<MP, RW, KW, NESTED, MH>;
+  auto kern = k_gemv<RW, KW, NESTED>;
   static const bool attr_done = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kXBudgetBytes + 4096 + kMaxWaves * kTBufBytes);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kGemvLdsMax);
     (void)hipGetLastError();
     return true;
   }();
   (void)attr_done;
-  const size_t need = gemv_lds_bytes(MP, RW, KW, p.M, p.kc);
-  const dim3 grid(static_cast<unsigned>((p.w.N + RW * MP - 1) / (RW * MP)),
+  const size_t need = gemv_region_bytes(32, RW, KW, p.M, p.kc);
+  const dim3 grid(static_cast<unsigned>((p.w.N + RW * 32 - 1) / (RW * 32)),
                   static_cast<unsigned>(p.splits));
   kern<<<grid, 64 * RW * KW, need, stream>>>(p);
   return hipGetLastError();
@@ -775,14 +719,13 @@ hipError_t launch_ln_kw(int kw, const GemvParams& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <int MP, int RW, bool NESTED, int MH>
-hipError_t launch_kw(int kw, const GemvParams& p, hipStream_t stream) {
+// 32-row groups: four per workgroup, 1, 2 or 4 contraction slices
+template <bool NESTED>
+hipError_t launch_kw32(int kw, const GemvParams& p, hipStream_t stream) {
   switch (kw) {
-    case 1: return launch_gemv_t<MP, RW, 1, NESTED, MH>(p, stream);
-    case 2: return launch_gemv_t<MP, RW, 2, NESTED, MH>(p, stream);
-    case 4: return launch_gemv_t<MP, RW, 4, NESTED, MH>(p, stream);
-    case 8: if constexpr (RW <= 2) return launch_gemv_t<MP, RW, 8, NESTED, MH>(p, stream); break;
-    case 16: if constexpr (RW == 1 && MH == 1) return launch_gemv_t<MP, RW, 16, NESTED, MH>(p, stream); break;
+    case 1: return launch_gemv_t<4, 1, NESTED>(p, stream);
+    case 2: return launch_gemv_t<4, 2, NESTED>(p, stream);
+    case 4: return launch_gemv_t<4, 4, NESTED>(p, stream);
     default: break;
   }
   return hipErrorInvalidValue;
@@ -886,8 +829,11 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   const bool nested = w.nested();
   const int kw = plan.consumers;
   if (plan.bm == 16) {
-    // line-staged kernel; two halves of x per expanded fragment above M = 16
-    if (plan.bn * kw > kLnMaxWaves || gemv_ln_lds_bytes(plan.bn, kw, M, plan.kc) > kLnLdsMax)
+    // line-staged kernel; two halves of x per expanded fragment above M = 16.
+    // A chunk of at most kLnMaxChunkSteps steps keeps each lane within two
+    // nested groups (the LDS budget of the x chunk already bounds it at 63).
+    if (plan.bn * kw > kLnMaxWaves || gemv_ln_lds_bytes(plan.bn, kw, M, plan.kc) > kLnLdsMax ||
+        plan.kc > 256 * kLnMaxChunkSteps)
       return hipErrorInvalidValue;
     p.tb_off = static_cast<int32_t>(gemv_region_bytes(16, plan.bn, kw, M, plan.kc));
     if (M > 16) {
@@ -901,12 +847,11 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
     if (plan.bn == 4) return nested ? launch_ln_kw<4, true, 1>(kw, p, stream) : launch_ln_kw<4, false, 1>(kw, p, stream);
     return hipErrorInvalidValue;
   }
-  if (gemv_lds_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc) >
-      static_cast<size_t>(kXBudgetBytes + 4096 + kMaxWaves * kTBufBytes))
+  // 32-row groups
+  if (plan.bm != 32 || plan.bn != 4 || gemv_region_bytes(32, 4, kw, M, plan.kc) > kGemvLdsMax)
     return hipErrorInvalidValue;
-  p.tb_off = static_cast<int32_t>(gemv_region_bytes(plan.bm, plan.bn, plan.consumers, M, plan.kc));
-  if (plan.bn == 4) return nested ? launch_kw<32, 4, true, 1>(kw, p, stream) : launch_kw<32, 4, false, 1>(kw, p, stream);
-  return hipErrorInvalidValue;
+  p.tb_off = 0;
+  return nested ? launch_kw32<true>(kw, p, stream) : launch_kw32<false>(kw, p, stream);
 }
 
 }  // namespace nf4

@@ -168,3 +168,42 @@ def test_tiled_step_counts(steps, bm, bn, consumers, plan_override):
     assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16)), "not bitwise repeatable"
     assert_close(gx, O.matmul_bwd_input(gyb, wb), f"grad_x steps={steps}",
                  O.matmul_bwd_input(abs_bits(gyb), abs_bits(wb)), N)
+
+
+def _weights(N, K, seed):
+    w = WL.weight_f32(N, K, WL.W_TINY, seed)
+    ref = O.quantize_nf4(w, nested=True)
+    return upload(ref, N, K, True), ref_bits(ref, (N, K))
+
+
+@pytest.mark.parametrize("bm,bn,consumers", [(256, 256, 0), (256, 128, 0), (256, 256, 4), (128, 128, 1),
+                                             (64, 128, 1), (128, 128, 6)])
+@pytest.mark.parametrize("steps", [1, 2, 3])
+def test_nested_first_steps_repeat(bm, bn, consumers, steps, plan_override):
+    """Nested statistics and contractions of one to three steps, so every read
+    of a copied scale comes right after the prologue: a hundred launches in a
+    row are bitwise equal in both directions and the first matches the
+    oracle.  (Consecutive steps' nested scales share an address; no counted
+    wait may pass before the older copy of it has landed.)"""
+    plan_override(bm, bn, consumers, 1)
+    bk = 64 if bm == 256 else 128                      # contraction depth of one step
+    M, N, K = 200, 392, steps * bk
+    wq, wb = _weights(N, K, 1200 + 10 * steps + consumers)
+    x = WL.x_bf16(M, K, WL.W_TINY, 1201 + steps)
+    xd = x.to(DEV)
+    ys = [api.nf4_matmul_fwd(xd, wq) for _ in range(100)]
+    torch.cuda.synchronize()
+    for i, y in enumerate(ys):
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16)), f"forward call {i} differs"
+    xb = WL.bf16_bits(x)
+    assert_close(ys[0], O.matmul_fwd(xb, wb), "y", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+    N2, K2 = steps * bk, 192
+    wq2, wb2 = _weights(N2, K2, 1300 + 10 * steps + consumers)
+    gy = WL.grad_y_bf16(M, N2, WL.W_TINY, 1301 + steps)
+    gyd = gy.to(DEV)
+    gs = [api.nf4_matmul_bwd_input(gyd, wq2) for _ in range(100)]
+    torch.cuda.synchronize()
+    for i, g in enumerate(gs):
+        assert torch.equal(g.view(torch.int16), gs[0].view(torch.int16)), f"input gradient call {i} differs"
+    gyb = WL.bf16_bits(gy)
+    assert_close(gs[0], O.matmul_bwd_input(gyb, wb2), "grad_x", O.matmul_bwd_input(abs_bits(gyb), abs_bits(wb2)), N2)
