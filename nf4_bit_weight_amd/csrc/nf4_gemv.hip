@@ -350,13 +350,15 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv(GemvParams p) {
 // copied per step: a chunk holds at most 64 steps, so a lane's blocks span
 // fewer than 256 and meet at most two nested groups, whose two scales the
 // lane loads into registers once, before its first copy.  Two slots
-// per wave keep a workgroup's LDS small enough that the launches of the
-// decode shapes are resident in one round (measured: four slots halved the
-// resident workgroups and made the forward of gate at M = 1 18 us instead of
-// 15).  The buffer resources carry the tensor bounds (reads past the end
+// per wave keep a workgroup's LDS small (three or four were measured
+// slower, see kSD).  The buffer resources carry the tensor bounds (reads past the end
 // return zero) and move with the step in scalar registers: the loop computes
 // no vector addresses.
-constexpr int kSD = 2;                          // staging slots per wave = copy distance (steps)
+// Staging slots per wave = copy distance in steps (2 to 4 supported).
+// Measured on the Llama-3.1-8B decode passes: three slots made the forward
+// of gate 15.0 us instead of 13.2-14.1 at M = 1 and 21.4 instead of 17.3 at
+// M = 8, four slots 17.0 and 22.4 (the larger workgroups fit fewer per CU).
+constexpr int kSD = 2;
 constexpr int kSlotBytes = 2048 + 256;          // packed lines, block scales
 constexpr int kLnMaxChunkSteps = 64;            // chunk length bound the nested-scale pair relies on
 constexpr int kLnMaxWaves = 8;
@@ -371,6 +373,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   const int32_t n = (hi | (lo >> 31)) != 0 ? 0x7FFFFFFF : static_cast<int32_t>(lo);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
                                            kRsrcWord3);
+}
+
+// s_waitcnt vmcnt(V), lgkmcnt and expcnt left open (gfx9 field layout)
+template <int V>
+__device__ __forceinline__ void vm_wait_open() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (15 << 8) | (7 << 4));
 }
 
 template <int RW, int KW, bool NESTED, int MH>
@@ -431,13 +440,24 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, 4u * lane_b, 0, 0, 0);
     }
   };
+  // Wait until at most the copies of `later` steps (C instructions each) are
+  // in flight: vmcnt(C * later) with lgkmcnt and expcnt left open.
+  static_assert(kSD >= 2 && kSD <= 4, "wait counts and step loop below");
+  auto wait_later = [&](int later) {
+    switch (later) {
+      case 0: vm_wait_open<0>(); break;
+      case 1: vm_wait_open<C>(); break;
+      case 2: vm_wait_open<2 * C>(); break;
+      case 3: vm_wait_open<3 * C>(); break;
+      default: vm_wait_open<4 * C>(); break;
+    }
+  };
   // Before step ls: the copies of step ls have landed once at most those of
-  // the later step already issued (ls + 1; none before the last step) are in
-  // flight.  vmcnt(c) with lgkmcnt and expcnt left open.
-  static_assert(kSD == 2, "wait counts below");
+  // the later steps already issued (ls + 1 .. ls + kSD - 1, within the run)
+  // are in flight.
   auto wait_copies = [&](int ls) {
-    if (ls + 1 < nw) __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | (15 << 8) | (7 << 4));
-    else __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));
+    const int later = nw - 1 - ls < kSD - 1 ? nw - 1 - ls : kSD - 1;
+    wait_later(later);
   };
   auto fence = [] {
     asm volatile("" ::: "memory");
@@ -511,13 +531,12 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
   // keep the count behind every step uniform, read stale data in 2-22% of
   // runs after its counted wait; with exact counts and no repeated copy in
   // flight, 0 of 200.)
-  if (nw > 0) issue(0, 0);
-  if (nw > 1) issue(1, 1);
+#pragma unroll
+  for (int j = 0; j < kSD; ++j)
+    if (j < nw) issue(j, j);
   fence();
   // the x and table loads have returned once at most this wave's copies are in flight
-  if (nw > 1) __builtin_amdgcn_s_waitcnt(((2 * C) & 15) | (((2 * C) >> 4) << 14) | (15 << 8) | (7 << 4));
-  else if (nw == 1) __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | (15 << 8) | (7 << 4));
-  else __builtin_amdgcn_s_waitcnt((15 << 8) | (7 << 4));
+  wait_later(nw < kSD ? nw : kSD);
   if constexpr (NESTED) {
 #pragma unroll
     for (int j = 0; j < kNC; ++j)
@@ -565,10 +584,12 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
                : "memory")
   auto read_slot = [&](auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
-    static_assert(kSlotBytes == 2304 && kSD == 2, "slot offsets below");
+    static_assert(kSlotBytes == 2304 && kSD <= 4, "slot offsets below");
     Staged u;
     if constexpr (slot == 0) NF4_LN_READ(0);
-    else NF4_LN_READ(2304);
+    else if constexpr (slot == 1) NF4_LN_READ(2304);
+    else if constexpr (slot == 2) NF4_LN_READ(4608);
+    else NF4_LN_READ(6912);
     return u;
   };
 #undef NF4_LN_READ
@@ -611,11 +632,19 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
     fence();
   };
   int s = 0;
-  for (; s + 2 <= nw; s += 2) {
+  for (; s + kSD <= nw; s += kSD) {
     one(s, ic<0>{});
     one(s + 1, ic<1>{});
+    if constexpr (kSD > 2) one(s + 2, ic<2>{});
+    if constexpr (kSD > 3) one(s + 3, ic<3>{});
   }
   if (s < nw) one(s, ic<0>{});
+  if constexpr (kSD > 2) {
+    if (s + 1 < nw) one(s + 1, ic<1>{});
+  }
+  if constexpr (kSD > 3) {
+    if (s + 2 < nw) one(s + 2, ic<2>{});
+  }
 
   // ---- fixed-order sum over the KW contraction slices of each row group ------
   constexpr int kRegs = 4 * MH;

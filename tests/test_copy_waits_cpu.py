@@ -1,6 +1,6 @@
 """Copy waits of the kernels that count their own copies, checked on the host
 against their issue order: the producer/consumer tiles, the register-operand
-forward and the ping-pong tiles.
+forward, the ping-pong tiles and the line-staged small-M forward.
 
 The producer waves of the (BM x BN) tiled kernel issue LDS-direct copies that
 complete in issue order and wait on them with vmcnt(c), i.e. until at most c of
@@ -234,3 +234,96 @@ def test_ping_pong_replay_catches_a_short_wait():
     ex["end"] = {**ex["end"], 2: 3}             # one copy more left in flight than the newest weights
     with pytest.raises(AssertionError, match="end of step"):
         _replay_pp(1, 2, 6, ex)
+
+
+# Line-staged small-M kernel (nf4_gemv.hip): each wave issues C LDS-direct
+# copies per step into kSD private slots, kSD steps ahead; the prologue issues
+# the copies of steps 0 .. kSD - 1 after the x and table loads and waits until
+# only those copies are in flight; before step ls the wave waits until at most
+# the copies of `later` steps are in flight, and after it refills the slot of
+# step ls with step ls + kSD.  Step ls reads slot ls % kSD.
+
+GEMV_SRC = os.path.join(ROOT, "nf4_bit_weight_amd", "csrc", "nf4_gemv.hip")
+
+
+def _ln_exprs():
+    s = open(GEMV_SRC).read()
+    body = s[s.index("void k_gemv_ln(GemvParams p)"):s.index("size_t gemv_region_bytes(")]
+    sd = re.search(r"constexpr int kSD = (\d+);", s)
+    c = re.search(r"constexpr int C = (\d+);", body)
+    cases = dict(re.findall(r"case (\d+): vm_wait_open<([^>]+)>\(\); break;", body))
+    dflt = re.search(r"default: vm_wait_open<([^>]+)>\(\); break;", body)
+    later = re.search(r"auto wait_copies = \[&\]\(int ls\) \{\s*const int later = ([^;]+);\s*wait_later\(later\);", body)
+    pro = re.search(r"for \(int j = 0; j < kSD; \+\+j\)\s*if \(j < nw\) issue\(j, j\);\s*fence\(\);[^\n]*\n[^\n]*\n"
+                    r"\s*wait_later\(([^;]+)\);", body)
+    refill = re.search(r"if \(ls \+ kSD < nw\) issue\(ls \+ kSD, slot\);", body)
+    issue = body[body.index("auto issue = [&](int ls, int slot)"):body.index("auto wait_later")]
+    assert sd and c and cases and dflt and later and pro and refill, "line-staged copy and wait code not found"
+    # copies per issue: two packed-line copies, then one scale copy in either form
+    assert issue.count("raw_ptr_buffer_load_lds(") == 4 and "if constexpr (NESTED)" in issue
+    conv = lambda e: re.sub(r"\(?([^()?]+)\?([^():]+):([^()]+)\)?", r"((\2) if (\1) else (\3))", e)
+    return {"kSD": int(sd.group(1)), "C": int(c.group(1)), "cases": {int(k): v for k, v in cases.items()},
+            "default": dflt.group(1), "later": conv(later.group(1)), "pro": conv(pro.group(1))}
+
+
+def _replay_ln(nw, ex):
+    kSD, C = ex["kSD"], ex["C"]
+    ops, done = [], 0
+    issued = set()
+
+    def ev(e, **kw):
+        return eval(e, {"__builtins__": {}}, {"kSD": kSD, "C": C, "nw": nw, **kw})
+
+    def vmcnt(later):
+        return ev(ex["cases"].get(later, ex["default"]))
+
+    def issue(step):
+        assert step not in issued, f"step {step} copied twice"
+        issued.add(step)
+        ops.extend([("W", step)] * C)
+
+    def wait(c):
+        nonlocal done
+        done = max(done, len(ops) - c)
+
+    def landed(kind, step):
+        return max(k for k, o in enumerate(ops) if o == (kind, step)) < done
+
+    ops.extend([("X", 0)] * 5)                         # x batch and table loads
+    for j in range(kSD):
+        if j < nw:
+            issue(j)
+    wait(vmcnt(ev(ex["pro"])))
+    assert landed("X", 0), "prologue: x and tables before they are stored"
+    slot = {}
+    for j in range(min(kSD, nw)):
+        slot[j % kSD] = j
+    for ls in range(nw):
+        wait(vmcnt(ev(ex["later"], ls=ls)))
+        assert landed("W", ls), f"before step {ls}: its copies"
+        assert slot[ls % kSD] == ls, f"step {ls}: slot holds step {slot[ls % kSD]}"
+        if ls + kSD < nw:
+            issue(ls + kSD)
+            slot[ls % kSD] = ls + kSD
+    assert issued == set(range(nw))
+
+
+def test_line_staged_copy_waits_cover_every_read():
+    ex = _ln_exprs()
+    for nw in range(0, 70):
+        _replay_ln(nw, ex)
+
+
+@pytest.mark.parametrize("kSD", [2, 3, 4])
+def test_line_staged_waits_hold_for_every_slot_count(kSD):
+    """The wait code is written for 2 to 4 slots; each count is replayed."""
+    ex = {**_ln_exprs(), "kSD": kSD}
+    for nw in range(0, 40):
+        _replay_ln(nw, ex)
+
+
+def test_line_staged_replay_catches_a_short_wait():
+    ex = _ln_exprs()
+    ex["later"] = "(kSD if nw - 1 - ls > kSD else nw - 1 - ls)"   # one step more left in flight
+    with pytest.raises(AssertionError, match="before step"):
+        _replay_ln(8, ex)
