@@ -1486,7 +1486,11 @@ __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restr
 //
 // Tile BM x 128 (BM = 128, 64 or 32), BK = 64 (8-bit) or 128 (NF4): every
 // thread owns 32 weight bytes of a step.  Four waves (2 x 2 of 64 x 64, or
-// 1 x 4 of BM x 32), v_mfma_f32_32x32x16_bf16.  Every step the threads load
+// 1 x 4 of BM x 32), or eight (NF4: 2 x 4 of 64 x 32 or 32 x 32), with
+// v_mfma_f32_32x32x16_bf16.  NF4 also as 128 x 256 with eight waves of
+// 64 x 64 and BK = 64: per MFMA two thirds of the fragment reads of the
+// 128 x 128 eight-wave tile, whose LDS reads bound its multiply part; its
+// grouped form serves experts of up to 128 rows.  Every step the threads load
 // the next step's activation vectors and weight bytes into registers, the
 // waves multiply the current LDS buffers, and the threads then store the
 // activations and expand their weights into the other buffer; one barrier
@@ -1495,11 +1499,15 @@ __global__ __launch_bounds__(kThreads) void k_splitk_reduce(const float* __restr
 // stores its weights one element per output-column row, the NF4 input
 // gradient [contraction][128 + 16] (whole 16-byte stores), read with
 // ds_read_b64_tr_b16 as in the producer/consumer kernel.
-template <int BITS, int BM, int NW>
+template <int BITS, int BM, int NW, int BN_ = 128>
 struct GT {
   static_assert(NW == 4 || (NW == 8 && BITS == 4 && BM >= 64), "8 waves: NF4, 64 or 128 rows");
+  static_assert(BN_ == 128 || (BN_ == 256 && BITS == 4 && NW == 8 && BM == 128),
+                "256 columns: NF4, 8 waves, 128 rows");
   static constexpr int kThreads = 64 * NW;
-  static constexpr int BN = 128, BK = BITS == 8 ? 64 : 128, kPitch = BK + 8, kPitchT = BN + 16;
+  // 256 columns take 64-deep steps: two buffers of 128 x 128 and 256 x 128
+  // would not fit the LDS
+  static constexpr int BN = BN_, BK = (BITS == 8 || BN_ == 256) ? 64 : 128, kPitch = BK + 8, kPitchT = BN + 16;
   static constexpr int WAVES_M = (BM == 128 || NW == 8) ? 2 : 1, WAVES_N = NW / WAVES_M;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int MI = WM / 32, NI = WN / 32;
@@ -1515,9 +1523,9 @@ struct GT {
   static constexpr int kLds(bool trans) { return 2 * (kA + kB(trans)) * 2; }
 };
 
-template <int BITS, int BM, int NW, bool TRANS, bool NESTED, bool GROUPED>
+template <int BITS, int BM, int NW, int BN_, bool TRANS, bool NESTED, bool GROUPED>
 __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
-  using G = GT<BITS, BM, NW>;
+  using G = GT<BITS, BM, NW, BN_>;
   constexpr int BN = G::BN, BK = G::BK, P = G::kPitch, PT = G::kPitchT;
   constexpr bool TR = G::kTrRead(TRANS);
   constexpr int KB = G::kB(TRANS);
@@ -1838,10 +1846,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
   }
 }
 
-template <int BITS, int BM, int NW, bool TRANS, bool NESTED, bool GROUPED>
+template <int BITS, int BM, int NW, int BN_, bool TRANS, bool NESTED, bool GROUPED>
 hipError_t launch_gt(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipStream_t stream) {
-  using G = GT<BITS, BM, NW>;
-  auto kern = k_gemmt<BITS, BM, NW, TRANS, NESTED, GROUPED>;
+  using G = GT<BITS, BM, NW, BN_>;
+  auto kern = k_gemmt<BITS, BM, NW, BN_, TRANS, NESTED, GROUPED>;
   constexpr int lds = G::kLds(TRANS);
   static const bool attr_done = [&] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1861,22 +1869,24 @@ hipError_t launch_gt(const GemmParams& p, int64_t m_tiles, int64_t n_cols, hipSt
   return hipGetLastError();
 }
 
-// Register-staged tiles: BM = 32, 64 or 128 (8-bit: 32 or 128); NF4 with 4
-// waves, or 8 waves at 64 and 128 rows.
+// Register-staged tiles: BM = 32, 64 or 128 (8-bit: 32 or 128) by 128
+// columns; NF4 with 4 waves, or 8 waves at 64 and 128 rows; NF4 128 x 256
+// with 8 waves.
 template <int BITS, bool TRANS, bool GROUPED>
-hipError_t dispatch_gt(int bm, int nw, const GemmParams& p, int64_t m_tiles, int64_t n_cols,
+hipError_t dispatch_gt(int bm, int nw, int bn, const GemmParams& p, int64_t m_tiles, int64_t n_cols,
                        hipStream_t stream) {
   const bool nested = p.w.nested();
-#define NF4_GT(BMV, NWV)                                                                           \
-  if (bm == BMV && nw == NWV)                                                                      \
-    return nested ? launch_gt<BITS, BMV, NWV, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)    \
-                  : launch_gt<BITS, BMV, NWV, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
-  NF4_GT(32, 4)
-  NF4_GT(128, 4)
+#define NF4_GT(BMV, NWV, BNV)                                                                        \
+  if (bm == BMV && nw == NWV && bn == BNV)                                                           \
+    return nested ? launch_gt<BITS, BMV, NWV, BNV, TRANS, true, GROUPED>(p, m_tiles, n_cols, stream) \
+                  : launch_gt<BITS, BMV, NWV, BNV, TRANS, false, GROUPED>(p, m_tiles, n_cols, stream);
+  NF4_GT(32, 4, 128)
+  NF4_GT(128, 4, 128)
   if constexpr (BITS == 4) {
-    NF4_GT(64, 4)
-    NF4_GT(64, 8)
-    NF4_GT(128, 8)
+    NF4_GT(64, 4, 128)
+    NF4_GT(64, 8, 128)
+    NF4_GT(128, 8, 128)
+    NF4_GT(128, 8, 256)
   }
 #undef NF4_GT
   return hipErrorInvalidValue;
@@ -1951,8 +1961,7 @@ hipError_t dispatch_tile(int bm, int bn, int c, const GemmParams& p, int64_t m_t
                   : launch_tiled<BMV, BNV, TRANS, false, GROUPED, CV>(p, m_tiles, n_cols, stream);   \
   }
   if (c == kStagedTile || c == kStagedTile8) {
-    if (bn != 128) return hipErrorInvalidValue;
-    return dispatch_gt<4, TRANS, GROUPED>(bm, c == kStagedTile8 ? 8 : 4, p, m_tiles, n_cols, stream);
+    return dispatch_gt<4, TRANS, GROUPED>(bm, c == kStagedTile8 ? 8 : 4, bn, p, m_tiles, n_cols, stream);
   }
   if (bm == 256 && bn == 256 && c == 0) {
     return nested ? launch_pp<TRANS, true, GROUPED>(p, m_tiles, n_cols, stream)
@@ -2053,15 +2062,17 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
   if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
   if (staged_mid && o_bm == 0 && o_bn == 0 && o_c == 0) pl.consumers = kStagedTile8;
-  // NF4_CONSUMERS=5: the register-staged tile kernel, 128 columns, NF4_BM
-  // rows (32, 64 or 128; default 128)
+  // NF4_CONSUMERS=5/6: the register-staged tile kernel with 4 / 8 waves, 128
+  // columns, NF4_BM rows (32, 64 or 128; default 128); 6 with NF4_BN=256:
+  // 128 x 256
   if (o_c == kStagedTile || o_c == kStagedTile8) {
     pl.consumers = o_c;
     pl.bn = 128;
     pl.bm = (o_bm == 64 || (o_bm == 32 && o_c == kStagedTile)) ? o_bm : 128;
+    if (o_c == kStagedTile8 && o_bn == 256) { pl.bn = 256; pl.bm = 128; }
   }
   const bool staged = pl.consumers == kStagedTile || pl.consumers == kStagedTile8;
-  const int bk = (pl.consumers == 3) ? 64 : (staged ? 128 : 16384 / pl.bn);
+  const int bk = (pl.consumers == 3) ? 64 : (staged ? (pl.bn == 256 ? 64 : 128) : 16384 / pl.bn);
   const int64_t tiles = ((M + pl.bm - 1) / pl.bm) * ((nc + pl.bn - 1) / pl.bn);
   const int64_t ksteps = (kc + bk - 1) / bk;
   // Split count: minimise (rounds of workgroups over the compute units) x
@@ -2125,14 +2136,16 @@ GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int3
   // rows per expert are only known on the device; size the tile by the mean
   const int64_t mean = (E > 0) ? (total_M + E - 1) / E : total_M;
   if (mean <= 128) {
-    // Few rows per expert: the 8-wave register-staged 128 x 128 tile, one row
+    // Few rows per expert: the 8-wave register-staged 128 x 256 tile, one row
     // tile per expert of up to 128 rows, each weight expanded once per
     // expert.  Measured on MI355X with 64 experts of 46-86 rows (OLMoE
-    // shapes): gate/up 63 / 79 us forward / input gradient, down 72 / 66 us,
-    // against 98 / 100 and 76 / 95 us with 256-row register-operand and
-    // ping-pong tiles.
+    // shapes): gate/up 52.7 / 64.0 us forward / input gradient, down
+    // 55.7 / 54.3 us, against 63.0 / 75.5 and 65.8 / 59.9 us with 128 x 128
+    // (64 x 32 per wave: a third more LDS fragment reads per MFMA) and
+    // 98 / 100 and 76 / 95 us with 256-row register-operand and ping-pong
+    // tiles.
     pl.bm = 128;
-    pl.bn = 128;
+    pl.bn = 256;
     pl.consumers = kStagedTile8;
   } else {
     pl.bm = mean <= 192 ? 128 : 256;
@@ -2151,6 +2164,7 @@ GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int3
       pl.consumers = o_c;
       pl.bn = 128;
       pl.bm = (o_bm == 64 || (o_bm == 32 && o_c == kStagedTile)) ? o_bm : 128;
+      if (o_c == kStagedTile8 && o_bn == 256) { pl.bn = 256; pl.bm = 128; }
     }
   }
   return pl;
@@ -2264,8 +2278,8 @@ hipError_t launch_gemm8(GemmKind kind, const GemmPlan& plan, const void* A, int6
   p.E = 1;
   p.splits = plan.splits;
   const int64_t m_tiles = (M + plan.bm - 1) / plan.bm;
-  hipError_t e = trans ? dispatch_gt<8, true, false>(plan.bm, 4, p, m_tiles, nc, stream)
-                       : dispatch_gt<8, false, false>(plan.bm, 4, p, m_tiles, nc, stream);
+  hipError_t e = trans ? dispatch_gt<8, true, false>(plan.bm, 4, 128, p, m_tiles, nc, stream)
+                       : dispatch_gt<8, false, false>(plan.bm, 4, 128, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 9 : 8);
   if (plan.splits > 1) {
@@ -2297,8 +2311,8 @@ hipError_t launch_grouped8(GemmKind kind, const void* A, const int32_t* offsets,
   p.E = E;
   p.splits = 1;
   const int64_t m_tiles = (total_M + bm - 1) / bm + E;
-  hipError_t e = trans ? dispatch_gt<8, true, true>(bm, 4, p, m_tiles, nc, stream)
-                       : dispatch_gt<8, false, true>(bm, 4, p, m_tiles, nc, stream);
+  hipError_t e = trans ? dispatch_gt<8, true, true>(bm, 4, 128, p, m_tiles, nc, stream)
+                       : dispatch_gt<8, false, true>(bm, 4, 128, p, m_tiles, nc, stream);
   if (e != hipSuccess) return e;
   count_path(trans ? 9 : 8);
   return hipSuccess;

@@ -50,7 +50,7 @@ struct GemmPlan {
   size_t ws_bytes; // fp32 partials when splits > 1
 };
 constexpr int kStagedTile = 5;    // 4 waves
-constexpr int kStagedTile8 = 6;   // 8 waves (NF4, 64 or 128 rows)
+constexpr int kStagedTile8 = 6;   // 8 waves (NF4, 64 or 128 rows; 128 x 256)
 int device_cu_count();
 GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus);
 GemmPlan plan_grouped(GemmKind kind, int64_t total_M, int64_t N, int64_t K, int32_t E);

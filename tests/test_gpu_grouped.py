@@ -110,7 +110,7 @@ def test_olmoe_experts(proj):
 @pytest.mark.parametrize("bm,bn,consumers", [(64, 256, 1), (64, 128, 1), (128, 256, 1), (128, 256, 2),
                                              (128, 128, 1), (256, 256, 4), (256, 256, 0), (256, 128, 0),
                                              (128, 128, 5), (64, 128, 5), (32, 128, 5),
-                                             (128, 128, 6), (64, 128, 6)])
+                                             (128, 128, 6), (64, 128, 6), (128, 256, 6)])
 def test_grouped_tiles(bm, bn, consumers):
     """Every tile the grouped products can be given through NF4_BM / NF4_BN /
     NF4_CONSUMERS, on ragged experts (empty ones, one spanning two 128-row
@@ -154,7 +154,7 @@ def test_grouped_tiles(bm, bn, consumers):
 
 
 @pytest.mark.parametrize("bm,bn,consumers", [(0, 0, 0), (64, 128, 1), (256, 256, 4), (256, 128, 0),
-                                             (128, 128, 5), (128, 128, 6)])
+                                             (128, 128, 5), (128, 128, 6), (128, 256, 6)])
 def test_grouped_many_experts(bm, bn, consumers):
     """150 experts (three rounds of the 64-lane expert search), many of them
     empty, several spanning two or three row tiles: every row lands in its

@@ -21,10 +21,10 @@ pytestmark = pytest.mark.gpu
 # consumer kernel; 256 x 128 is the 4-wave register-operand forward (the input
 # gradient falls back to 256 x 256).  Smaller tiles: MFMA waves per SIMD beside
 # the expanding wave; 5 = the register-staged tile kernel (128 columns, 128,
-# 64 or 32 rows), 6 = the same with 8 waves (128 or 64 rows).
+# 64 or 32 rows), 6 = the same with 8 waves (128 or 64 rows, or 128 x 256).
 TILES = [(256, 256, 0), (256, 128, 0), (256, 256, 4), (256, 256, 2), (128, 256, 1), (128, 256, 2),
          (64, 256, 1), (128, 128, 1), (64, 128, 1), (128, 128, 5), (64, 128, 5), (32, 128, 5),
-         (128, 128, 6), (64, 128, 6)]
+         (128, 128, 6), (64, 128, 6), (128, 256, 6)]
 
 
 @pytest.fixture
@@ -129,7 +129,7 @@ RING_TILES = [(256, 256, 2), (128, 256, 1), (128, 256, 2), (64, 256, 1), (128, 1
 PP_TILES = [(256, 256, 4), (256, 256, 0)]
 # The register-staged tile kernel (4 or 8 waves): 128-deep steps, the next step's operands
 # held in registers, two LDS buffers.
-STAGED_TILES = [(128, 128, 5), (64, 128, 5), (32, 128, 5), (128, 128, 6), (64, 128, 6)]
+STAGED_TILES = [(128, 128, 5), (64, 128, 5), (32, 128, 5), (128, 128, 6), (64, 128, 6), (128, 256, 6)]
 
 
 @pytest.mark.parametrize("steps", [1, 2, 3, 4, 5, 6, 7, 10, 11, 13])
@@ -177,7 +177,7 @@ def _weights(N, K, seed):
 
 
 @pytest.mark.parametrize("bm,bn,consumers", [(256, 256, 0), (256, 128, 0), (256, 256, 4), (128, 128, 1),
-                                             (64, 128, 1), (128, 128, 6)])
+                                             (64, 128, 1), (128, 128, 6), (128, 256, 6)])
 @pytest.mark.parametrize("steps", [1, 2, 3])
 def test_nested_first_steps_repeat(bm, bn, consumers, steps, plan_override):
     """Nested statistics and contractions of one to three steps, so every read
@@ -186,7 +186,7 @@ def test_nested_first_steps_repeat(bm, bn, consumers, steps, plan_override):
     oracle.  (Consecutive steps' nested scales share an address; no counted
     wait may pass before the older copy of it has landed.)"""
     plan_override(bm, bn, consumers, 1)
-    bk = 64 if bm == 256 else 128                      # contraction depth of one step
+    bk = 64 if 256 in (bm, bn) else 128                # contraction depth of one step
     M, N, K = 200, 392, steps * bk
     wq, wb = _weights(N, K, 1200 + 10 * steps + consumers)
     x = WL.x_bf16(M, K, WL.W_TINY, 1201 + steps)
