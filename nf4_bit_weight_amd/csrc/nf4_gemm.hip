@@ -1519,15 +1519,31 @@ struct GT {
   static constexpr int kAVec = BM * BK / 8 / kThreads;         // activation vectors per thread
   static constexpr int kDepth = 4;                             // steps held in registers
   static constexpr bool kTrRead(bool trans) { return BITS == 4 && trans; }
-  static constexpr int kB(bool trans) { return kTrRead(trans) ? BK * kPitchT : BN * kPitch; }
+  // Eight waves: the transposed tile has unpadded rows whose 16-byte units
+  // are XOR-swizzled by the row (256 columns: as in the ping-pong kernel; 128
+  // columns: unit ^ 5 (row & 3)), so that the expansion's 16-byte writes (16
+  // lanes) and the transposed 8-byte reads (32 lanes) each hit 64 distinct
+  // banks.  Measured on the padded pitch (BN + 16): both were 2-way
+  // conflicted, and the conflicts were more than half of the 128 x 256 input
+  // gradient's LDS cycles.
+  static constexpr bool kSwzT = NW == 8;
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (BN_ == 256) return PP::swz_t(r);
+    else return 5 * (r & 3);
+  }
+  static constexpr int kB(bool trans) {
+    return kTrRead(trans) ? BK * (kSwzT ? BN : kPitchT) : BN * kPitch;
+  }
   static constexpr int kLds(bool trans) { return 2 * (kA + kB(trans)) * 2; }
 };
 
 template <int BITS, int BM, int NW, int BN_, bool TRANS, bool NESTED, bool GROUPED>
 __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
   using G = GT<BITS, BM, NW, BN_>;
-  constexpr int BN = G::BN, BK = G::BK, P = G::kPitch, PT = G::kPitchT;
+  constexpr int BN = G::BN, BK = G::BK, P = G::kPitch;
   constexpr bool TR = G::kTrRead(TRANS);
+  constexpr bool SWZ = TR && G::kSwzT;
+  constexpr int PT = SWZ ? BN : G::kPitchT;             // row pitch of the transposed tile
   constexpr int KB = G::kB(TRANS);
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ float scode[BITS == 8 ? 256 : 1];
@@ -1601,8 +1617,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
   // tensor and get a zero scale.
   constexpr int kTpr = (TRANS ? BN : BK) / G::PW;       // threads per W row of the step
   static_assert(kTpr * (TRANS ? BK : BN) == G::kThreads, "one piece per thread");
-  const int wl = tid / kTpr;
-  const int wq = tid % kTpr;
+  // (swizzled 256-column transposed tile: thread t takes half t & 1 of unit
+  // t >> 1, W row (t >> 1) % 64 of the step, columns 64 ((t >> 1) / 64) +
+  // 32 (t & 1), the write pattern its swizzle spreads over distinct banks;
+  // 128 columns keep the mapping below, four threads per W row)
+  constexpr bool kPPMap = SWZ && BN == 256;
+  static_assert(!kPPMap || (kTpr == 8 && BK == 64 && G::kThreads == 512), "swizzled mapping below");
+  static_assert(!SWZ || kPPMap || kTpr == 4, "128-column swizzle: four threads per W row");
+  const int wl = kPPMap ? ((tid >> 1) & 63) : tid / kTpr;
+  const int wq = kPPMap ? (((tid >> 7) << 1) | (tid & 1)) : tid % kTpr;
   const int64_t kblocks = K / 64;
   struct Regs {
     u32x4_t a[G::kAVec];
@@ -1676,8 +1699,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
     } else {
       uint32_t o[4];
       expand8_eo(wd, lt, o);
-      uint16_t* dst = TRANS ? bb + wl * PT + G::PW * wq : bb + wl * P + G::PW * wq;
-      *reinterpret_cast<u32x4_t*>(dst + 8 * d) = u32x4_t{o[0], o[1], o[2], o[3]};
+      uint16_t* dst;
+      if constexpr (SWZ) dst = bb + wl * PT + 8 * ((4 * wq + d) ^ G::swz(wl));
+      else dst = (TRANS ? bb + wl * PT + G::PW * wq : bb + wl * P + G::PW * wq) + 8 * d;
+      *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{o[0], o[1], o[2], o[3]};
     }
   };
   auto make_table = [&](float a) __attribute__((always_inline)) {
@@ -1703,10 +1728,19 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
     for (int j = 0; j < G::NI; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  // transposed-read lane offset: rows 8 (g >> 1) + (s >> 2) (+ 4), columns
-  // 16 (g & 1) + 4 (s & 3) of each 32-column fragment (g = lane / 16, s = lane % 16)
-  const int tr_off = (8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * PT + wn * G::WN +
-                     16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // transposed-read lane offsets: rows 8 (g >> 1) + (s >> 2) (+ 4 for the
+  // upper half; + 16 per slice, which keeps row & 7 and so the swizzle),
+  // columns 16 (g & 1) + 4 (s & 3) of 32-column fragment j (g = lane / 16,
+  // s = lane % 16)
+  int tr_o[G::NI][2];
+#pragma unroll
+  for (int j = 0; j < G::NI; ++j)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = 8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2) + 4 * hf;
+      const int col = wn * G::WN + 16 * ((lane >> 4) & 1) + 4 * (lane & 3) + 32 * j;
+      tr_o[j][hf] = SWZ ? row * PT + 8 * ((col >> 3) ^ G::swz(row)) + (col & 7) : row * PT + col;
+    }
   // a wave whose rows all lie past the tile's last row skips its MFMAs
   const bool active = row0 + wm * G::WM < row_end;
   struct Frags {
@@ -1720,9 +1754,9 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < G::NI; ++j) {
       if constexpr (TR) {
-        const uint16_t* src = b_buf(buf) + tr_off + 16 * kk * PT + 32 * j;
-        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 4 * PT));
+        const uint16_t* src = b_buf(buf) + 16 * kk * PT;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + tr_o[j][0]));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + tr_o[j][1]));
         const u32x2_t ul = __builtin_bit_cast(u32x2_t, lo), uh = __builtin_bit_cast(u32x2_t, hi);
         f.b[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{ul[0], ul[1], uh[0], uh[1]});
       } else {
