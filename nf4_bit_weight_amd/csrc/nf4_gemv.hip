@@ -364,9 +364,9 @@ constexpr int kLnMaxChunkSteps = 64;            // chunk length bound the nested
 constexpr int kLnMaxWaves = 8;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
 
-// `bytes` > 0 (every copy starts inside its tensor); sizes from 2 GiB up are
-// clamped (the offsets a wave uses stay far below).  The test is on the high
-// bits so that it stays a scalar instruction.
+// `bytes` >= 0 (a copy starts inside its tensor, or its resource is empty);
+// sizes from 2 GiB up are clamped (the offsets a wave uses stay far below).
+// The test is on the high bits so that it stays a scalar instruction.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const uint64_t b = static_cast<uint64_t>(bytes);
   const uint32_t hi = static_cast<uint32_t>(b >> 32), lo = static_cast<uint32_t>(b);
@@ -423,21 +423,37 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
   const uint32_t lane_b = static_cast<uint32_t>(r * kb + g);      // block of the lane within the step
   uint8_t* const slots = reinterpret_cast<uint8_t*>(xs) + p.tb_off + wave * (kSD * kSlotBytes);
 
+  // A copy reads only bytes of the wave's own rows and steps: a row group past
+  // N gets an empty resource, and on a step that ends past the row (K not a
+  // multiple of 256) the pieces and blocks past the row's end get an offset
+  // beyond the resource, so they read zero without a memory access instead
+  // of the head of the next row (which another wave of the workgroup copies:
+  // two copies of the same bytes in flight must not happen, see above).
+  constexpr uint32_t kNoRead = 0x80000000u;                  // beyond any resource's size
+  const int gp0 = piece(lr, lane & 7), gp1 = piece(8 + lr, lane & 7);   // 32-element piece of each row
   auto issue = [&](int ls, int slot) {
     const int st = s_begin + ls;                             // 0 <= st < nsteps
     const int64_t kstep = k0 + 256 * static_cast<int64_t>(st);
     uint8_t* const sl = slots + slot * kSlotBytes;
+    const bool live = rg0 < N;
     const int64_t wb = (rg0 * K + kstep) >> 1;               // first byte of the step's lines
-    const auto rw_ = rsrc(p.w.packed + wb, ((N * K) >> 1) - wb);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)sl, 16, voff_w0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)(sl + 1024), 16, voff_w1, 0, 0, 0);
+    const auto rw_ = rsrc(p.w.packed + (live ? wb : 0), live ? ((N * K) >> 1) - wb : 0);
+    uint32_t v0 = voff_w0, v1 = voff_w1, vb = NESTED ? lane_b : 4u * lane_b;
+    if (kstep + 256 > K) {                                   // the row ends inside this step
+      const int lim = static_cast<int>((K - kstep) >> 5);   // pieces left in the row (even)
+      v0 = gp0 < lim ? v0 : kNoRead;
+      v1 = gp1 < lim ? v1 : kNoRead;
+      vb = 2 * g < lim ? vb : kNoRead;                       // block g: pieces 2g, 2g + 1
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)sl, 16, v0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)(sl + 1024), 16, v1, 0, 0, 0);
     const int64_t bb = rg0 * kb + (kstep >> 6);              // block of lane 0
     if constexpr (NESTED) {
-      const auto ra = rsrc(static_cast<const uint8_t*>(p.w.absmax) + bb, nb - bb);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 1, lane_b, 0, 0, 0);
+      const auto ra = rsrc(static_cast<const uint8_t*>(p.w.absmax) + (live ? bb : 0), live ? nb - bb : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 1, vb, 0, 0, 0);
     } else {
-      const auto ra = rsrc(static_cast<const float*>(p.w.absmax) + bb, 4 * (nb - bb));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, 4u * lane_b, 0, 0, 0);
+      const auto ra = rsrc(static_cast<const float*>(p.w.absmax) + (live ? bb : 0), live ? 4 * (nb - bb) : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, vb, 0, 0, 0);
     }
   };
   // Wait until at most the copies of `later` steps (C instructions each) are

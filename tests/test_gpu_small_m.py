@@ -204,3 +204,37 @@ def test_small_m_nested_first_steps_repeat(M, N, K):
         assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16)), f"call {i} differs"
     xb = WL.bf16_bits(x)
     assert_close(ys[0], O.matmul_fwd(xb, wb), f"y {M}x{N}x{K}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+
+
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("rw,kw", [("4", "2"), ("1", "4"), ("2", "2")])
+@pytest.mark.parametrize("M,N,K", [(5, 300, 1600), (1, 136, 1088), (8, 264, 320)])
+def test_small_m_ragged_rows_repeat(M, N, K, rw, kw, nested):
+    """K not a multiple of the 256-column step, so each row ends inside the
+    last step, with several contraction slices and row groups per workgroup
+    and N ragged (row groups past N): fifty calls in a row are bitwise equal
+    and the first matches the oracle.  (Covers the copies of a last step that
+    ran on into the head of the next row, which another wave of the workgroup
+    copied in the same window.)"""
+    wq, wb, x = _setup(M, N, K, nested, 13 * M + N + K + int(rw) + int(kw))
+    keys = ("NF4_GEMV_KW", "NF4_GEMV_RW")
+    old = {k: os.environ.get(k) for k in keys}
+    os.environ["NF4_GEMV_KW"], os.environ["NF4_GEMV_RW"] = kw, rw
+    try:
+        xd = x.to(DEV)
+        api.nf4_reset_path_counts()
+        ys = [api.nf4_matmul_fwd(xd, wq) for _ in range(50)]
+        torch.cuda.synchronize()
+        c = api.nf4_path_counts()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert c["fwd_small_m"] == 50
+    for i, y in enumerate(ys):
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16)), f"call {i} differs"
+    xb = WL.bf16_bits(x)
+    assert_close(ys[0], O.matmul_fwd(xb, wb), f"y {M}x{N}x{K} rw={rw} kw={kw}",
+                 O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
