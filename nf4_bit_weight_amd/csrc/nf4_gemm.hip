@@ -424,7 +424,10 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         uint32_t o[4];
-        expand8(d < 4 ? pk0[d] : pk1[d - 4], lt, o);
+        // input gradient: the unit's 8 weights are 8 output columns, so the
+        // cheaper (0,2,4,6,1,3,5,7) order is undone in the epilogue
+        if constexpr (TRANS) expand8_eo(d < 4 ? pk0[d] : pk1[d - 4], lt, o);
+        else expand8(d < 4 ? pk0[d] : pk1[d - 4], lt, o);
         *reinterpret_cast<u32x4_t*>(b_dst(buf, d)) = u32x4_t{o[0], o[1], o[2], o[3]};
       }
     };
@@ -620,12 +623,15 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
   }
 
   // ---- epilogue ----------------------------------------------------------------
-  // acc[i][j][v] holds C[32i + 8(v/4) + 4h + v%4][32j + r32] of the wave tile.
+  // acc[i][j][v] holds C[32i + 8(v/4) + 4h + v%4][32j + r32] of the wave tile
+  // (input gradient: tile column c is output column 8 (c / 8) + pi(c % 8), the
+  // order of expand8_eo).
 #pragma unroll
   for (int i = 0; i < T::MI; ++i) {
 #pragma unroll
     for (int j = 0; j < T::NI; ++j) {
-      const int64_t col = col0 + wn * T::WN + 32 * j + r32;
+      int64_t col = col0 + wn * T::WN + 32 * j + r32;
+      if constexpr (TRANS) col = (col & ~int64_t{7}) | (((col & 3) << 1) | ((col >> 2) & 1));
       if (col >= Nc) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -879,7 +885,10 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       uint32_t o[4];
-      expand8(r.pk[d], lt, o);
+      // input gradient: 8 output columns per dword, in the (0,2,4,6,1,3,5,7)
+      // order that the epilogue undoes
+      if constexpr (TRANS) expand8_eo(r.pk[d], lt, o);
+      else expand8(r.pk[d], lt, o);
       *reinterpret_cast<u32x4_t*>(b_dst(buf, d)) = u32x4_t{o[0], o[1], o[2], o[3]};
       if (with_dma) dma(d);
     }
@@ -1117,7 +1126,9 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
   for (int i = 0; i < PP::MI; ++i) {
 #pragma unroll
     for (int j = 0; j < PP::NI; ++j) {
-      const int64_t col = col0 + wn * PP::WN + 32 * j + r32;
+      int64_t col = col0 + wn * PP::WN + 32 * j + r32;
+      // input gradient: tile column c is output column 8 (c / 8) + pi(c % 8)
+      if constexpr (TRANS) col = (col & ~int64_t{7}) | (((col & 3) << 1) | ((col >> 2) & 1));
       if (col >= Nc) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
