@@ -2061,7 +2061,15 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // The streaming kernel addresses a 16-row group of W with 32-bit offsets:
   // rows of up to 2^26 elements.
   const char* sm = getenv("NF4_SMALL_M");
-  if (kind == GemmKind::kFwd && M <= 32 && K <= (int64_t{1} << 26) && !(sm && sm[0] == '0')) {
+  // Above M = 24 the large products take the 8-wave 64-row register-staged
+  // tile instead (measured on MI355X over the Llama-3.1-8B projections at
+  // M = 32: gate 24.1 against 26.6 us, down 23.4 against 25.5 us; q and k,
+  // 15.8 / 14.2 against 14.7 / 13.0 us, and every product at M = 16 and 24
+  // but the input-width down, stay with the streaming kernels)
+  const bool staged_small = kind == GemmKind::kFwd && M > 24 && M <= 32 &&
+                            static_cast<double>(N) * static_cast<double>(K) >= 33554432.0;
+  if (kind == GemmKind::kFwd && M <= 32 && K <= (int64_t{1} << 26) && !(sm && sm[0] == '0') &&
+      !staged_small) {
     plan_small_m(pl, M, N, K, cus);
     return pl;
   }
@@ -2085,6 +2093,8 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   const bool staged_mid = M >= 256 && M <= 1024 && macs >= 6e9 && macs < 1.6e10;
   if (staged_mid) {
     pl.bm = 128; pl.bn = 128;
+  } else if (staged_small) {
+    pl.bm = 64; pl.bn = 128;
   } else if ((macs >= 2e10 || (macs >= 4e9 && (kind == GemmKind::kFwd || 2 * tiles256 >= cus))) && M > 128) {
     pl.bm = 256; pl.bn = 256;
   } else if (macs >= 4e9 && M > 64) {
@@ -2106,7 +2116,7 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // the ping-pong kernel for the forward too
   pl.consumers = (pl.bm == 256) ? (o_c == 2 ? 2 : (kind == GemmKind::kFwd && o_c != 4 ? 3 : 0)) : 1;
   if (o_c == 2 && pl.bm == 128 && pl.bn == 256) pl.consumers = 2;
-  if (staged_mid && o_bm == 0 && o_bn == 0 && o_c == 0) pl.consumers = kStagedTile8;
+  if ((staged_mid || staged_small) && o_bm == 0 && o_bn == 0 && o_c == 0) pl.consumers = kStagedTile8;
   // NF4_CONSUMERS=5/6: the register-staged tile kernel with 4 / 8 waves, 128
   // columns, NF4_BM rows (32, 64 or 128; default 128); 6 with NF4_BN=256:
   // 128 x 256
