@@ -2061,12 +2061,13 @@ GemmPlan plan_gemm(GemmKind kind, int64_t M, int64_t N, int64_t K, int cus) {
   // The streaming kernel addresses a 16-row group of W with 32-bit offsets:
   // rows of up to 2^26 elements.
   const char* sm = getenv("NF4_SMALL_M");
-  // Above M = 24 the large products take the 8-wave 64-row register-staged
-  // tile instead (measured on MI355X over the Llama-3.1-8B projections at
-  // M = 32: gate 24.1 against 26.6 us, down 23.4 against 25.5 us; q and k,
-  // 15.8 / 14.2 against 14.7 / 13.0 us, and every product at M = 16 and 24
-  // but the input-width down, stay with the streaming kernels)
-  const bool staged_small = kind == GemmKind::kFwd && M > 24 && M <= 32 &&
+  // Above M = 16 the large products take the 8-wave 64-row register-staged
+  // tile instead (measured on MI355X over the Llama-3.1-8B projections,
+  // gate / down: at M = 32 24.1 / 23.4 against 26.6 / 25.5 us, at M = 20
+  // 23.3 / 23.4 against 24.3 / 28.2, at M = 24 23.6 / 23.2 against
+  // 22.9 / 27.7; q and k, 15.8 / 14.2 against 14.7 / 13.0 us at M = 32, stay
+  // with the streaming kernels, as does every product up to M = 12)
+  const bool staged_small = kind == GemmKind::kFwd && M > 16 && M <= 32 &&
                             static_cast<double>(N) * static_cast<double>(K) >= 33554432.0;
   if (kind == GemmKind::kFwd && M <= 32 && K <= (int64_t{1} << 26) && !(sm && sm[0] == '0') &&
       !staged_small) {

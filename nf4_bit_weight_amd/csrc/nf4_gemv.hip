@@ -41,7 +41,8 @@ namespace nf4 {
 namespace {
 
 constexpr int kPD = 4;                    // packed-weight prefetch distance (steps)
-constexpr int kXBudgetBytes = 64 * 1024;  // LDS for the staged x chunk (M + 1 rows)
+constexpr int kXBudgetBytes = 64 * 1024;  // LDS for a staged x chunk (M + 1 rows) ...
+constexpr int kXWholeBytes = 96 * 1024;   // ... or for the whole of x in one chunk
 constexpr int kMaxWaves = 16;
 
 struct GemvParams {
@@ -710,7 +711,7 @@ size_t gemv_region_bytes(int mp, int rw, int kw, int64_t M, int kc) {
   const size_t rb = static_cast<size_t>(kw - 1) * rw * regs * 64 * 4;
   return ((xb > rb ? xb : rb) + 15) / 16 * 16;
 }
-constexpr size_t kGemvLdsMax = kXBudgetBytes + 4096;
+constexpr size_t kGemvLdsMax = kXWholeBytes + 4096;
 
 template <int RW, int KW, bool NESTED>
 hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
@@ -733,7 +734,7 @@ hipError_t launch_gemv_t(const GemvParams& p, hipStream_t stream) {
 size_t gemv_ln_lds_bytes(int rw, int kw, int64_t M, int kc) {
   return gemv_region_bytes(16, rw, kw, M, kc) + static_cast<size_t>(rw) * kw * kSD * kSlotBytes;
 }
-constexpr size_t kLnLdsMax = kXBudgetBytes + 4096 + kLnMaxWaves * kSD * kSlotBytes;
+constexpr size_t kLnLdsMax = kXWholeBytes + 4096 + kLnMaxWaves * kSD * kSlotBytes;
 
 template <int RW, int KW, bool NESTED, int MH>
 hipError_t launch_ln_t(const GemvParams& p, hipStream_t stream) {
@@ -796,8 +797,18 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   pl.bm = (M > 16 && mp32) ? 32 : 16;
   const int step = pl.bm == 16 ? 256 : 128;
   // largest chunk whose x (M + 1 rows, padded) fits the LDS budget
+  // Chunks of x within 64 KB of LDS, or all of x in one chunk (no split of
+  // the contraction, no partials) when it fits in 96 KB.  Measured over the
+  // Llama-3.1-8B decode projections: the single chunk takes q / gate at M = 8
+  // from 10.4 / 17.5 to 8.3 / 15.7 us and down at M = 2 from 16.0 to 14.0,
+  // while chunks of up to 96 KB where x is larger made down at M = 4 24.3
+  // instead of 18.3 us and q at M = 32 17.6 instead of 14.6.
+  const int64_t k_all = (K + step - 1) / step * step;
   int64_t kx = (kXBudgetBytes / 2 / (M + 1) - 8) / step * step;
+  if ((M + 1) * (k_all + 8) * 2 <= kXWholeBytes) kx = k_all;
   if (kx < step) kx = step;
+  // the line-staged kernel's chunks hold at most kLnMaxChunkSteps steps
+  if (pl.bm == 16 && kx > 256 * kLnMaxChunkSteps) kx = 256 * kLnMaxChunkSteps;
   int64_t z = (K + kx - 1) / kx;
   // tuning override (documented): NF4_GEMV_Z raises the chunk count
   const char* oz = getenv("NF4_GEMV_Z");
@@ -828,9 +839,13 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
     while (kw < 8 && steps > 16 * kw) kw *= 2;
   } else {
     // (at M = 16 the forward of q takes 11.2 us with four row groups, 15.3
-    // with one; at M = 8 one row group and 8 slices are best for it, 9.9 us)
+    // with one; at M = 8 one row group and 8 slices are best for it, 9.9 us;
+    // from M = 2 four row groups pay once their workgroups cover three
+    // quarters of the compute units: gate at M = 2 / 4 13.9 / 14.6 us
+    // against 16.4 / 19.5 with one, while down at M = 2, 128 such
+    // workgroups, takes 23.0 against 16.3)
     const int64_t wgs4 = (rg16 + 3) / 4 * z;
-    if (M > 4 && (wgs4 >= cus || (M > 8 && 2 * wgs4 >= cus))) rw = 4;
+    if (M > 1 && (4 * wgs4 >= 3 * static_cast<int64_t>(cus) || (M > 8 && 2 * wgs4 >= cus))) rw = 4;
     if (rw == 4) {
       kw = 2;
     } else {
@@ -876,7 +891,7 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   if (plan.bm == 16) {
     // line-staged kernel; two halves of x per expanded fragment above M = 16.
     // A chunk of at most kLnMaxChunkSteps steps keeps each lane within two
-    // nested groups (the LDS budget of the x chunk already bounds it at 63).
+    // nested groups (plan_small_m caps the chunk there).
     if (plan.bn * kw > kLnMaxWaves || gemv_ln_lds_bytes(plan.bn, kw, M, plan.kc) > kLnLdsMax ||
         plan.kc > 256 * kLnMaxChunkSteps)
       return hipErrorInvalidValue;
