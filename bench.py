@@ -322,8 +322,9 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
     comp["layer_total"]["fused_tflops"] = round(flops_layer / (tot["fused_us"] * 1e-6) / 1e12, 1)
     comp["layer_total"]["dense_only_tflops"] = round(flops_layer / (tot["dense_only_us"] * 1e-6) / 1e12, 1)
     comp["layer_total"]["today_tflops"] = round(flops_layer / (tot["dequant_plus_dense_us"] * 1e-6) / 1e12, 1)
-    # decode sizes, forward only: the streaming kernel against dequantise +
-    # dense GEMV/GEMM, summed over layer 0's seven projections
+    # decode sizes, forward only: the fused forward (the streaming kernels, or
+    # the 64-row staged tiles for the large products above M = 16) against
+    # dequantise + dense GEMV/GEMM, summed over layer 0's seven projections
     for Md in WL.DECODE_MS:
         t = {f"{n}_us": 0.0 for n in arm_names}
         rels, ran = [], True
@@ -345,7 +346,8 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
             api.nf4_matmul_fwd(x, w, out=y_f, ws=ws_c)
             y_c = F.linear(x, wd_r)
             torch.cuda.synchronize()
-            ran = ran and api.nf4_path_counts()["fwd_small_m"] == 1
+            pc = api.nf4_path_counts()
+            ran = ran and pc["fwd_small_m"] + pc["fwd_tiled"] == 1
             rels.append(float((y_f.float() - y_c.float()).norm().item() / max(y_c.float().norm().item(), 1e-30)))
             del x, ws_c, wd, wd_r, y_f, y_c
         comp[f"decode_M={Md}_fwd"] = {k: round(v, 1) for k, v in t.items()}
