@@ -1224,16 +1224,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
     a_colofs[j] = 8 * swz(r, a_unit);
   }
   auto stage_ptr = [&](int stage) { return lds + stage * R::kAElems; };
+  // copy j (8 rows) of the wave's part of the activation tile of step i < n
+  auto issue_a_one = [&](int i, int stage, int j) __attribute__((always_inline)) {
+    const int64_t c0 = static_cast<int64_t>(kb + i) * BK;
+    int64_t col = c0 + a_colofs[j];
+    col = col < K ? col : K - 8;
+    const uint16_t* src = a_row_ptr[j] + col;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_ptr(stage) + (R::kARows * wave + 8 * j) * BK), 16, 0, 0);
+  };
   auto issue_a = [&](int i, int stage) __attribute__((always_inline)) {
-    const int kt = kb + (i < n ? i : n - 1);
-    const int64_t c0 = static_cast<int64_t>(kt) * BK;
 #pragma unroll
-    for (int j = 0; j < kAJ; ++j) {
-      int64_t col = c0 + a_colofs[j];
-      col = col < K ? col : K - 8;
-      const uint16_t* src = a_row_ptr[j] + col;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage_ptr(stage) + (R::kARows * wave + 8 * j) * BK), 16, 0, 0);
-    }
+    for (int j = 0; j < kAJ; ++j) issue_a_one(i, stage, j);
   };
 
   // ---- weight copies: lane l fetches the 16 bytes it expands (W row
@@ -1246,8 +1247,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
   const uint8_t* const pk_base = p.w.packed + ((wrow_g * K) >> 1) + 16 * h;
   const int64_t blocks_per_row = K / BK;
   char* const w_area = reinterpret_cast<char*>(lds) + R::kWOff;
-  auto issue_w = [&](int i, int slot) __attribute__((always_inline)) {
-    const int kt = kb + (i < n ? i : n - 1);
+  auto issue_w = [&](int i, int slot) __attribute__((always_inline)) {   // step i < n
+    const int kt = kb + i;
     char* sl = w_area + slot * R::kWSlot + wave * R::kWWave;
     const uint8_t* src = row_ok ? pk_base + static_cast<int64_t>(kt) * (BK / 2) : p.w.packed;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)sl, 16, 0, 0);
@@ -1323,16 +1324,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
   };
 
   // ---- pipeline ---------------------------------------------------------------------
-  // Copies of step j: activation in the step j-2 issue, weights in the step
-  // j-3 issue; step i's issue goes out right after its barrier.
+  // Copies of step j: the activation tile during step j-2, the weights during
+  // step j-3 (the prologue issues W0 A0 W1 A1 W2).  Only copies of steps that
+  // exist are issued: a second copy of bytes already in flight could let a
+  // counted wait pass before the first one has landed, so every wait below
+  // counts exactly the copies issued after the one it needs.  Within a step
+  // the copies go out between the MFMA groups of its slices (activation
+  // copies in slices 0-2, the weights in slice 3): issued in one burst at the
+  // step's start they held the wave at the issue for ~800 of ~3000 cycles
+  // per step (per-phase timestamps), with no MFMA in flight.
   if (n > 0) {
     if constexpr (NESTED) __syncthreads();         // sncode filled, before any copy is in flight
     issue_w(0, 0);
     issue_a(0, 0);
-    issue_w(1, 1);
-    issue_a(1, 1);
-    issue_w(2, 2);
-    wait_vm(ic<2 * kCopies>{});                    // weights of step 0 landed
+    if (n > 1) {
+      issue_w(1, 1);
+      issue_a(1, 1);
+    }
+    if (n > 2) issue_w(2, 2);
+    // weights of step 0 landed (issued after them: A0, and W1 A1 W2 where they exist)
+    if (n > 2) wait_vm(ic<2 * kCopies>{});
+    else if (n > 1) wait_vm(ic<kAJ + kCopies>{});
+    else wait_vm(ic<kAJ>{});
     {
       const Staged r = read_unit(ic<0>{});
       const Lut lt = make_lut(code, unit_scale(r));
@@ -1350,16 +1363,22 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
     // MFMAs are issued the wave waits for its part of A(i+1), joins the
     // barrier and reads slice 0 of step i+1 while those MFMAs still run.
     bf16x8_t f0[8], f1[8];
-    wait_vm(ic<kAJ + 2 * kWCopies>{});             // own part of A(0) landed (W(1), A(1), W(2) may fly)
+    // own part of A(0) landed (W1 A1 W2 may fly)
+    if (n > 2) wait_vm(ic<kAJ + 2 * kWCopies>{});
+    else if (n > 1) wait_vm(ic<kCopies>{});
+    else wait_vm(ic<0>{});
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     load_a(0, 0, f0);
-    auto step = [&](int i, auto ph) __attribute__((always_inline)) {
+    // FULL: a step with three more after it (every copy below exists; no
+    // branch splits its slices)
+    auto step = [&](int i, auto ph, auto full_c) __attribute__((always_inline)) {
       constexpr int P = decltype(ph)::value;       // i % 3
+      constexpr bool FULL = decltype(full_c)::value;
       __builtin_amdgcn_sched_barrier(0);
-      issue_a(i + 2, (P + 2) % 3);
-      issue_w(i + 3, P);
-      wait_vm(ic<2 * kCopies>{});                  // weights of step i+1 landed (batch i-2 done)
+      // weights of step i+1 landed (issued after them: A(i+1), W(i+2) where it exists)
+      if (FULL || i + 2 < n) wait_vm(ic<kCopies>{});
+      else if (i + 1 < n) wait_vm(ic<kAJ>{});
       asm volatile("" ::: "memory");
       const Staged r = read_unit(ic<(P + 1) % 3>{});
       // the nested-scale lookup waits on LDS: do it before the slice-1
@@ -1381,9 +1400,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
           expand8(r.pk[kk - 1], lt, o);
           bw[kk - 1] = __builtin_bit_cast(bf16x8_t, u32x4_t{o[0], o[1], o[2], o[3]});
         }
+        // this slice's share of the copies of step i: activation copies j
+        // with 3 j / kAJ == kk of A(i+2), in slice 3 the weights of step i+3
+        if (kk < 3 && (FULL || i + 2 < n)) {
+#pragma unroll
+          for (int j = 0; j < kAJ; ++j)
+            if ((3 * j) / kAJ == kk) issue_a_one(i + 2, (P + 2) % 3, j);
+        }
+        if (kk == 3 && (FULL || i + 3 < n)) issue_w(i + 3, P);
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // a copy, while there are any
           __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then up to five VALU
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -1395,22 +1423,29 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("" ::: "memory");
-      // A(i+1) was the first part of batch i-1: W(i+2) of that batch and all
-      // of batch i may still be in flight
-      wait_vm(ic<kCopies + kWCopies>{});
+      // own part of A(i+1) landed: issued after it, W(i+2), A(i+2) and W(i+3)
+      // where they exist
+      if (FULL || i + 3 < n) wait_vm(ic<kCopies + kWCopies>{});
+      else if (i + 2 < n) wait_vm(ic<kCopies>{});
+      else wait_vm(ic<0>{});
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       load_a((P + 1) % 3, 0, f0);                  // slice 0 of step i+1 (a re-read on the last step)
     };
     int i = 0;
-    for (; i + 3 <= n; i += 3) {
-      step(i, ic<0>{});
-      step(i + 1, ic<1>{});
-      step(i + 2, ic<2>{});
+    for (; i + 6 <= n; i += 3) {                   // steps i .. i+2 each have three more after them
+      step(i, ic<0>{}, std::true_type{});
+      step(i + 1, ic<1>{}, std::true_type{});
+      step(i + 2, ic<2>{}, std::true_type{});
     }
-    if (i < n) step(i, ic<0>{});
-    if (i + 1 < n) step(i + 1, ic<1>{});
+    for (; i + 3 <= n; i += 3) {
+      step(i, ic<0>{}, std::false_type{});
+      step(i + 1, ic<1>{}, std::false_type{});
+      step(i + 2, ic<2>{}, std::false_type{});
+    }
+    if (i < n) step(i, ic<0>{}, std::false_type{});
+    if (i + 1 < n) step(i + 1, ic<1>{}, std::false_type{});
     wait_vm(ic<0>{});                              // no copy outlives the workgroup
   }
 

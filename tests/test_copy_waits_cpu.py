@@ -98,68 +98,111 @@ def test_replay_catches_the_steady_state_wait_in_the_prologue():
 
 
 # ---- the register-operand forward kernel -------------------------------------------
-# Its producer work is done by every wave: per step i it issues the activation
-# copy of step i+2 and then the weight copy of step i+3 (into a 3-slot ring),
-# after a prologue W0 A0 W1 A1 W2.  Step i expands the weights of step i+1 and
-# ends with every wave's part of A(i+1) landed.
+# Its producer work is done by every wave: a prologue W0 A0 W1 A1 W2 (only the
+# steps that exist), then during step i the activation copy of step i+2 (in
+# slices 0-2) and the weight copy of step i+3 (in slice 3), again only for
+# steps that exist.  Step i first waits for the weights of step i+1 (it
+# expands them during its slices) and ends with its part of A(i+1) landed.
+# Each wait is a chain of cases by how many of the later copies exist; the
+# chains are read from the kernel source.
+
+def _chain(text, pattern):
+    m = re.search(pattern, text, re.S)
+    assert m, pattern
+    return m.group(1)
+
+
+def _cases(chain):
+    """`if (c1) wait_vm(ic<e1>{}); else if (c2) wait_vm(ic<e2>{}); else wait_vm(ic<e3>{});`
+    as [(condition or None, expression)]."""
+    out = []
+    for cond, expr in re.findall(r"(?:else\s+)?(?:if\s*\(([^)]*)\)\s*)?wait_vm\(ic<([^>]+)>\{\}\);", chain):
+        out.append((cond or None, expr))
+    assert out, chain
+    return out
+
 
 def _rb_exprs():
     s = open(SRC).read()
-    body = s[s.index("void k_rb("):]
-    return {
+    body = s[s.index("void k_rb("):s.index("// Fixed-order sum of split partials")]
+    ex = {
         "kcopies": _expr(body, r"constexpr int kCopies = ([^;]+);"),
-        "pro_w0": _expr(body, r"wait_vm\(ic<([^>]+)>\{\}\);\s*// weights of step 0 landed"),
-        "pro_a0": _expr(body, r"wait_vm\(ic<([^>]+)>\{\}\);\s*// own part of A\(0\) landed"),
-        "step_w": _expr(body, r"wait_vm\(ic<([^>]+)>\{\}\);\s*// weights of step i\+1 landed"),
-        "step_a": _expr(body, r"may still be in flight\s*wait_vm\(ic<([^>]+)>\{\}\);"),
+        "pro_w0": _cases(_chain(body, r"// weights of step 0 landed[^\n]*\n(.*?wait_vm\(ic<kAJ>\{\}\);)")),
+        "pro_a0": _cases(_chain(body, r"// own part of A\(0\) landed[^\n]*\n(.*?else wait_vm\(ic<0>\{\}\);)")),
+        "step_w": _cases(_chain(body, r"// weights of step i\+1 landed[^\n]*\n(.*?else if \(i \+ 1 < n\) wait_vm\(ic<[^>]+>\{\}\);)").replace("FULL || ", "")),
+        "step_a": _cases(_chain(body, r"// own part of A\(i\+1\) landed[^\n]*\n[^\n]*\n(.*?else wait_vm\(ic<0>\{\}\);)").replace("FULL || ", "")),
     }
+    # the copies of a step go out only for steps that exist
+    assert "if (kk < 3 && (FULL || i + 2 < n))" in body and "if (kk == 3 && (FULL || i + 3 < n)) issue_w(i + 3, P);" in body
+    # a FULL step (three more steps after it) takes the first case of each chain
+    assert "for (; i + 6 <= n; i += 3) {" in body
+    assert "if (n > 1) {\n      issue_w(1, 1);\n      issue_a(1, 1);\n    }\n    if (n > 2) issue_w(2, 2);" in body
+    return ex
 
 
 def _replay_rb(kAJ, kWCopies, n, ex):
-    env = {"kAJ": kAJ, "kWCopies": kWCopies}
+    env = {"kAJ": kAJ, "kWCopies": kWCopies, "n": n}
     env["kCopies"] = eval(ex["kcopies"], {"__builtins__": {}}, env)
-    ops, done = [], 0
+    ops, done, issued = [], 0, set()
 
     def issue(kind, step, count):
+        assert step < n, f"copy of step {step} past the end"
+        assert (kind, step) not in issued, f"{kind}({step}) copied twice"
+        issued.add((kind, step))
         ops.extend([(kind, step)] * count)
 
-    def wait(key):
+    def wait(key, **kw):
         nonlocal done
-        done = max(done, len(ops) - eval(ex[key], {"__builtins__": {}}, env))
+        for cond, expr in ex[key]:
+            if cond is None or eval(cond, {"__builtins__": {}}, {**env, **kw}):
+                done = max(done, len(ops) - eval(expr, {"__builtins__": {}}, env))
+                return
 
     def landed(kind, step):
         return max(k for k, o in enumerate(ops) if o == (kind, step)) < done
 
-    for kind, j in (("W", 0), ("A", 0), ("W", 1), ("A", 1), ("W", 2)):
-        issue(kind, j, kAJ if kind == "A" else kWCopies)
+    issue("W", 0, kWCopies)
+    issue("A", 0, kAJ)
+    if n > 1:
+        issue("W", 1, kWCopies)
+        issue("A", 1, kAJ)
+    if n > 2:
+        issue("W", 2, kWCopies)
     wait("pro_w0")
     assert landed("W", 0), "prologue: weights of step 0"
     wait("pro_a0")
     assert landed("A", 0), "prologue: activation tile of step 0"
     for i in range(n):
-        issue("A", i + 2, kAJ)
-        issue("W", i + 3, kWCopies)
-        wait("step_w")
+        wait("step_w", i=i)
         if i + 1 < n:
             assert landed("W", i + 1), f"step {i}: weights of step {i + 1}"
-        wait("step_a")
+        if i + 2 < n:
+            issue("A", i + 2, kAJ)
+        if i + 3 < n:
+            issue("W", i + 3, kWCopies)
+        wait("step_a", i=i)
         if i + 1 < n:
             assert landed("A", i + 1), f"end of step {i}: activation tile of step {i + 1}"
+    assert issued == {(k, j) for k in "AW" for j in range(n)}
 
 
 def test_register_operand_copy_waits_cover_every_read():
     ex = _rb_exprs()
     for kAJ in (1, 2, 4, 8):
         for kWCopies in (2, 3):
-            for n in range(1, 10):
+            for n in range(1, 12):
                 _replay_rb(kAJ, kWCopies, n, ex)
 
 
 def test_register_operand_replay_catches_a_short_wait():
     ex = dict(_rb_exprs())
-    ex["step_a"] = "kCopies + kWCopies + 1"
+    ex["step_a"] = [("i + 3 < n", "kCopies + kWCopies + 1")] + ex["step_a"][1:]
     with pytest.raises(AssertionError, match="activation tile"):
-        _replay_rb(2, 3, 4, ex)
+        _replay_rb(2, 3, 6, ex)
+    ex = dict(_rb_exprs())
+    ex["step_w"] = [("i + 2 < n", "kCopies + 1")] + ex["step_w"][1:]
+    with pytest.raises(AssertionError, match="weights of step"):
+        _replay_rb(2, 3, 6, ex)
 
 
 # ---- the ping-pong kernel ----------------------------------------------------------
