@@ -365,9 +365,9 @@ constexpr int kLnMaxChunkSteps = 64;            // chunk length bound the nested
 constexpr int kLnMaxWaves = 8;
 constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format (gfx9 family)
 
-// `bytes` >= 0 (a copy starts inside its tensor, or its resource is empty);
-// sizes from 2 GiB up are clamped (the offsets a wave uses stay far below).
-// The test is on the high bits so that it stays a scalar instruction.
+// `bytes` > 0 (every copy starts inside its tensor); sizes from 2 GiB up are
+// clamped (the offsets a wave uses stay far below).  The test is on the high
+// bits so that it stays a scalar instruction.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   const uint64_t b = static_cast<uint64_t>(bytes);
   const uint32_t hi = static_cast<uint32_t>(b >> 32), lo = static_cast<uint32_t>(b);
@@ -403,15 +403,17 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
   const int kc = p.kc;
   const int pitch = kc + 8;
 
-  // this wave's steps of the chunk: a contiguous run
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t rg0 = (static_cast<int64_t>(blockIdx.x) * RW + rw) * 16;   // first W row of the group
+
+  // this wave's steps of the chunk: a contiguous run (none for a row group
+  // past N, which the last workgroup of a launch with RW > 1 may hold: it
+  // copies and computes nothing, and stores nothing)
   const int nsteps = static_cast<int>((k1 - k0 + 255) / 256);
   const int per = (nsteps + KW - 1) / KW;
   const int s_begin = kw * per < nsteps ? kw * per : nsteps;
   const int s_end = s_begin + per < nsteps ? s_begin + per : nsteps;
-  const int nw = s_end - s_begin;
-
-  const int r = lane & 15, g = lane >> 4;
-  const int64_t rg0 = (static_cast<int64_t>(blockIdx.x) * RW + rw) * 16;   // first W row of the group
+  const int nw = rg0 < N ? s_end - s_begin : 0;
   const int64_t kb = K >> 6;                       // blocks per W row
   const int64_t nb = N * kb;
   const int64_t ng = (nb + kNestedBlock - 1) / kNestedBlock;
@@ -424,37 +426,26 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
   const uint32_t lane_b = static_cast<uint32_t>(r * kb + g);      // block of the lane within the step
   uint8_t* const slots = reinterpret_cast<uint8_t*>(xs) + p.tb_off + wave * (kSD * kSlotBytes);
 
-  // A copy reads only bytes of the wave's own rows and steps: a row group past
-  // N gets an empty resource, and on a step that ends past the row (K not a
-  // multiple of 256) the pieces and blocks past the row's end get an offset
-  // beyond the resource, so they read zero without a memory access instead
-  // of the head of the next row (which another wave of the workgroup copies:
-  // two copies of the same bytes in flight must not happen, see above).
-  constexpr uint32_t kNoRead = 0x80000000u;                  // beyond any resource's size
-  const int gp0 = piece(lr, lane & 7), gp1 = piece(8 + lr, lane & 7);   // 32-element piece of each row
+  // Every copy lies inside the wave's own rows and steps: the host launches
+  // this kernel only when K is a multiple of 256 and N of 16, so a step never
+  // runs past the end of a row into the next one (which another wave of the
+  // workgroup copies: two copies of the same bytes in flight must not
+  // happen, see above) and a row group is either whole or, past N, idle.
   auto issue = [&](int ls, int slot) {
     const int st = s_begin + ls;                             // 0 <= st < nsteps
     const int64_t kstep = k0 + 256 * static_cast<int64_t>(st);
     uint8_t* const sl = slots + slot * kSlotBytes;
-    const bool live = rg0 < N;
     const int64_t wb = (rg0 * K + kstep) >> 1;               // first byte of the step's lines
-    const auto rw_ = rsrc(p.w.packed + (live ? wb : 0), live ? ((N * K) >> 1) - wb : 0);
-    uint32_t v0 = voff_w0, v1 = voff_w1, vb = NESTED ? lane_b : 4u * lane_b;
-    if (kstep + 256 > K) {                                   // the row ends inside this step
-      const int lim = static_cast<int>((K - kstep) >> 5);   // pieces left in the row (even)
-      v0 = gp0 < lim ? v0 : kNoRead;
-      v1 = gp1 < lim ? v1 : kNoRead;
-      vb = 2 * g < lim ? vb : kNoRead;                       // block g: pieces 2g, 2g + 1
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)sl, 16, v0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)(sl + 1024), 16, v1, 0, 0, 0);
+    const auto rw_ = rsrc(p.w.packed + wb, ((N * K) >> 1) - wb);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)sl, 16, voff_w0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw_, (lds_void_t*)(sl + 1024), 16, voff_w1, 0, 0, 0);
     const int64_t bb = rg0 * kb + (kstep >> 6);              // block of lane 0
     if constexpr (NESTED) {
-      const auto ra = rsrc(static_cast<const uint8_t*>(p.w.absmax) + (live ? bb : 0), live ? nb - bb : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 1, vb, 0, 0, 0);
+      const auto ra = rsrc(static_cast<const uint8_t*>(p.w.absmax) + bb, nb - bb);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 1, lane_b, 0, 0, 0);
     } else {
-      const auto ra = rsrc(static_cast<const float*>(p.w.absmax) + (live ? bb : 0), live ? 4 * (nb - bb) : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, vb, 0, 0, 0);
+      const auto ra = rsrc(static_cast<const float*>(p.w.absmax) + bb, 4 * (nb - bb));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sl + 2048), 4, 4u * lane_b, 0, 0, 0);
     }
   };
   // Wait until at most the copies of `later` steps (C instructions each) are
@@ -795,6 +786,16 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   bool mp32 = M > 24 || (M > 16 && N * K >= (int64_t{32} << 20));
   if (o32 && (o32[0] == '0' || o32[0] == '1')) mp32 = o32[0] == '1';
   pl.bm = (M > 16 && mp32) ? 32 : 16;
+  // The line-staged kernel (16-row groups) copies whole 256-column steps of
+  // whole 16-row groups with LDS-direct loads under counted waits; it takes
+  // only shapes where each such copy lies inside its own rows (K a multiple
+  // of 256, N of 16: every Llama, Qwen and OLMoE projection).  Others run the
+  // 32-row kernel, whose ordinary loads need no such care.  (Two wrong
+  // results, once each in many runs, came from the ragged cases: a last
+  // step that copied the head of the next row, which another wave copied,
+  // and once, after that was fixed, at M = 7, N = 520, K = 1088 with no
+  // cause found.)
+  if (K % 256 != 0 || N % 16 != 0) pl.bm = 32;
   const int step = pl.bm == 16 ? 256 : 128;
   // largest chunk whose x (M + 1 rows, padded) fits the LDS budget
   // Chunks of x within 64 KB of LDS, or all of x in one chunk (no split of
@@ -889,6 +890,7 @@ hipError_t launch_gemv(const GemmPlan& plan, const void* x, int64_t M, const WAr
   const bool nested = w.nested();
   const int kw = plan.consumers;
   if (plan.bm == 16) {
+    if (w.K % 256 != 0 || w.N % 16 != 0) return hipErrorInvalidValue;   // whole steps and row groups only
     // line-staged kernel; two halves of x per expanded fragment above M = 16.
     // A chunk of at most kLnMaxChunkSteps steps keeps each lane within two
     // nested groups (plan_small_m caps the chunk there).

@@ -36,10 +36,10 @@ def _setup(M, N, K, nested, seed):
     return wq, wb, x
 
 
+@pytest.mark.parametrize("N,K", [(200, 576), (208, 512)])   # ragged (32-row kernel); whole steps and row groups
 @pytest.mark.parametrize("M", [1, 16, 17, 32])
 @pytest.mark.parametrize("nested", [False, True])
-def test_permutation_probe_small_m(M, nested):
-    N, K = 200, 576                      # ragged N; K ends inside a 256 step
+def test_permutation_probe_small_m(M, nested, N, K):
     w = WL.weight_f32(N, K, WL.W_DECODE, 40 + M)
     ref = O.quantize_nf4(w, nested=nested)
     wq = upload(ref, N, K, nested)
@@ -128,10 +128,12 @@ def test_llama_decode_shapes(M, idx):
 @pytest.mark.parametrize("z", [1, 3])
 def test_small_m_slices_and_chunks(M, rw, mp32, kw, z):
     """Every (row-group size, row groups, contraction slices, chunks) instance
-    of the streaming kernel through the documented overrides: slices past a
-    short contraction hold no steps, chunks end inside a step, N is ragged (and,
-    with four row groups, ends inside the workgroup's first row group)."""
-    N, K = 300, 1600
+    of the streaming kernels through the documented overrides: slices past a
+    short contraction hold no steps, and with four row groups the last
+    workgroup holds a row group past N.  (N and K are whole 16-row groups and
+    256-column steps, the shapes the 16-row kernel takes; chunks of the
+    32-row kernel end inside its steps.)"""
+    N, K = 304, 1536
     nested = (kw + z) % 2 == 0
     wq, wb, x = _setup(M, N, K, nested, 7 * kw + z + M)
     xb = WL.bf16_bits(x)
@@ -164,7 +166,7 @@ def test_small_m_slices_and_chunks(M, rw, mp32, kw, z):
 
 
 @pytest.mark.parametrize("kw", ["2", "4"])
-@pytest.mark.parametrize("N,K", [(136, 320), (144, 512), (144, 320)])
+@pytest.mark.parametrize("N,K", [(144, 256), (144, 512), (160, 768)])
 def test_small_m_one_step_waves_repeat(N, K, kw):
     """Contraction slices of one step each (and empty ones), nested scales:
     thirty calls in a row are bitwise equal and match the oracle.  (Covers the
@@ -189,7 +191,7 @@ def test_small_m_one_step_waves_repeat(N, K, kw):
     assert_close(ys[0], want, f"y {M}x{N}x{K} kw={kw}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1000, 4160), (1, 264, 1088), (8, 1000, 4160), (3, 520, 8192)])
+@pytest.mark.parametrize("M,N,K", [(1, 1008, 4096), (1, 272, 1024), (8, 1008, 4096), (3, 528, 8192)])
 def test_small_m_nested_first_steps_repeat(M, N, K):
     """Nested statistics, many short waves whose first steps start right after
     the prologue: a hundred calls in a row are bitwise equal and the first
@@ -208,13 +210,14 @@ def test_small_m_nested_first_steps_repeat(M, N, K):
 
 @pytest.mark.parametrize("nested", [False, True])
 @pytest.mark.parametrize("rw,kw", [("4", "2"), ("1", "4"), ("2", "2")])
-@pytest.mark.parametrize("M,N,K", [(5, 300, 1600), (1, 136, 1088), (8, 264, 320)])
+@pytest.mark.parametrize("M,N,K", [(5, 300, 1600), (1, 136, 1088), (8, 264, 320), (5, 304, 1536)])
 def test_small_m_ragged_rows_repeat(M, N, K, rw, kw, nested):
-    """K not a multiple of the 256-column step, so each row ends inside the
-    last step, with several contraction slices and row groups per workgroup
-    and N ragged (row groups past N): fifty calls in a row are bitwise equal
-    and the first matches the oracle.  (Covers the copies of a last step that
-    ran on into the head of the next row, which another wave of the workgroup
+    """Ragged shapes (K not a multiple of 256, N not of 16: the 32-row kernel
+    takes them) and whole-step shapes with a row group past N in the last
+    workgroup (the 16-row kernel), several contraction slices and row groups
+    per workgroup: fifty calls in a row are bitwise equal and the first
+    matches the oracle.  (The 16-row kernel once copied, on a ragged last
+    step, the head of the next row, which another wave of the workgroup
     copied in the same window.)"""
     wq, wb, x = _setup(M, N, K, nested, 13 * M + N + K + int(rw) + int(kw))
     keys = ("NF4_GEMV_KW", "NF4_GEMV_RW")
