@@ -47,6 +47,9 @@ def parse():
                          "forward gate projections of the step), qwen:bwd_down, olmoe:fwd_gate")
     ap.add_argument("--m", type=int, default=0,
                     help="with --only: rows of x (default: the workload's M, 512 or 2048)")
+    ap.add_argument("--code", default="nf4", choices=("nf4", "fp4", "int8", "fp8_e4m3"),
+                    help="with --only: the code table the weights are quantised with (int8 and fp8_e4m3 "
+                         "are the 8-bit blockwise formats)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="with --only: then run one plain device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -192,7 +195,8 @@ def workspace_for(torch, api, projs, Ms, dev):
     need = 16
     for M in Ms:
         for p in projs:
-            need = max(need, api.nf4_workspace_bytes(1, M, p.N, p.K), api.nf4_workspace_bytes(2, M, p.N, p.K))
+            # forward / input gradient, NF4 and 8-bit plans
+            need = max(need, *(api.nf4_workspace_bytes(op, M, p.N, p.K) for op in (1, 2, 5, 6)))
     return torch.empty(need, dtype=torch.uint8, device=dev)
 
 
@@ -354,9 +358,12 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
         comp[f"decode_M={Md}_fwd"].update({
             "speedup_vs_today": round(t["dequant_plus_dense_us"] / t["fused_us"], 2),
             "max_rel_fro_diff": float(f"{max(rels):.3g}"), "fused_kernels_ran": ran})
-    del filler
     extra["comparator_llama8b_layer0"] = comp
     log(f"comparator done: {comp['layer_total']}")
+
+    extra["code_tables_llama8b_layer0"] = run_code_tables(torch, api, WL, ncode, dev, stream, filler, ceil)
+    del filler
+    log(f"code tables done: {extra['code_tables_llama8b_layer0']['summary']}")
 
     extra["layer_streaming_llama8b_m512"] = run_streaming(torch, api, WL, dev, llama_weights, stream)
     log(f"streaming done: {extra['layer_streaming_llama8b_m512']}")
@@ -423,6 +430,82 @@ def run_extra(torch, api, WL, code, ncode, dev, llama_weights, stream):
         "timing": "per direction: median over 21 interleaved rounds of 5 passes over the three stacks",
     }
     return extra
+
+
+def run_code_tables(torch, api, WL, ncode, dev, stream, filler, ceil):
+    """The code-table variants of the same calls (Experts PR, "Commit 1",
+    quant_type table): nf4 and fp4 (16-entry tables, the same kernels) and the
+    8-bit blockwise int8 and fp8 e4m3 formats (one byte per weight, 256-entry
+    tables, the 8-bit register-staged tiles).  Layer 0's seven Llama-3.1-8B
+    projections are quantised from the same fp32 weights in each format (all
+    nested); per projection the four formats are interleaved round by round:
+    forward + input gradient at M = 512, forward at M = 1.  Figures are sums
+    over the projections.  Every call is also compared with the dense product
+    of its own dequantised weight, and the path counters with its kernels."""
+    import torch.nn.functional as F
+    tables = {"nf4": (WL.nf4_code_np(), 4), "fp4": (WL.fp4_code_np(), 4),
+              "int8": (WL.int8_code_np(), 8), "fp8_e4m3": (WL.fp8_e4m3_code_np(), 8)}
+    codes = {f: (torch.from_numpy(t).to(dev), b) for f, (t, b) in tables.items()}
+    M, projs = WL.LLAMA_M, WL.LLAMA_8B
+    res = {f: {"m512_fwd_bwd_us": 0.0, "m1_fwd_us": 0.0, "weight_bytes": 0, "max_rel_fro_diff": 0.0,
+               "kernels_ran": True} for f in tables}
+    for i, p in enumerate(projs):
+        wf = WL.gpu_weight_f32(p.N, p.K, seed=WL.stack_weight_seed(WL.LLAMA_STACK_W_SEED, 0, i), device=dev)
+        wq = {f: api.nf4_quantize(wf, c, ncode, bits=b) for f, (c, b) in codes.items()}
+        del wf
+        x = WL.gpu_normal_bf16(M, p.K, seed=93_000 + i, device=dev)
+        gy = WL.gpu_normal_bf16(M, p.N, seed=94_000 + i, device=dev)
+        x1 = WL.gpu_normal_bf16(1, p.K, seed=95_000 + i, device=dev)
+        wsb = workspace_for(torch, api, [p], [M, 1], dev)
+        y = torch.empty((M, p.N), dtype=torch.bfloat16, device=dev)
+        g = torch.empty((M, p.K), dtype=torch.bfloat16, device=dev)
+        y1 = torch.empty((1, p.N), dtype=torch.bfloat16, device=dev)
+
+        def fwd_bwd(w):
+            return lambda: (api.nf4_matmul_fwd(x, w, out=y, ws=wsb), api.nf4_matmul_bwd_input(gy, w, out=g, ws=wsb))
+
+        def fwd1(w):
+            return lambda: api.nf4_matmul_fwd(x1, w, out=y1, ws=wsb)
+
+        m512 = interleaved(torch, stream, {f: fwd_bwd(w) for f, w in wq.items()}, filler, rounds=11)
+        m1 = interleaved(torch, stream, {f: fwd1(w) for f, w in wq.items()}, filler, rounds=11)
+        for f, w in wq.items():
+            r = res[f]
+            r["m512_fwd_bwd_us"] += m512[f]["median_us"]
+            r["m1_fwd_us"] += m1[f]["median_us"]
+            r["weight_bytes"] += w.nbytes()
+            api.nf4_reset_path_counts()
+            fwd_bwd(w)()
+            fwd1(w)()
+            torch.cuda.synchronize()
+            pc = api.nf4_path_counts()
+            if w.bits == 8:
+                ok = pc["fwd_8bit"] == 2 and pc["bwd_8bit"] == 1
+            else:
+                ok = pc["fwd_tiled"] + pc["fwd_small_m"] == 2 and pc["bwd_tiled"] == 1
+            r["kernels_ran"] = r["kernels_ran"] and ok
+            wd = api.nf4_dequantize(w)
+            for got, ref in ((y, F.linear(x, wd)), (g, torch.matmul(gy, wd)), (y1, F.linear(x1, wd))):
+                rel = float((got.float() - ref.float()).norm().item() / max(ref.float().norm().item(), 1e-30))
+                r["max_rel_fro_diff"] = max(r["max_rel_fro_diff"], rel)
+            del wd
+        del wq, x, gy, x1, wsb, y, g, y1
+    flops = 2 * sum(2.0 * M * p.N * p.K for p in projs)
+    nweights = sum(p.N * p.K for p in projs)
+    out = {}
+    for f, r in res.items():
+        t5, t1 = r["m512_fwd_bwd_us"], r["m1_fwd_us"]
+        gbs = r["weight_bytes"] / (t1 * 1e-6) / 1e9
+        out[f] = {"m512_fwd_bwd_us": round(t5, 1), "m512_tflops": round(flops / (t5 * 1e-6) / 1e12, 1),
+                  "m512_frac_of_bf16_peak": round(flops / (t5 * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "m1_fwd_us": round(t1, 1), "m1_weight_GBps": round(gbs, 1),
+                  "m1_frac_of_copy_ceiling": round(gbs / ceil["GBps"], 4),
+                  "bytes_per_weight": round(r["weight_bytes"] / nweights, 4),
+                  "max_rel_fro_diff": float(f"{r['max_rel_fro_diff']:.3g}"), "kernels_ran": r["kernels_ran"]}
+    out["timing"] = ("per projection, the four formats interleaved: median over 11 rounds of 5 calls, each round "
+                     "after a 1 GiB filler copy; figures summed over the seven projections")
+    out["summary"] = {f: [out[f]["m512_tflops"], out[f]["m1_weight_GBps"]] for f in tables}
+    return out
 
 
 def run_streaming(torch, api, WL, dev, llama_weights, stream, slots=3):
@@ -646,7 +729,10 @@ def run_only(args):
         raise SystemExit(f"--only {args.only}: expected [llama:|qwen:|olmoe:](fwd|bwd)_<projection>")
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    code = torch.from_numpy(WL.nf4_code_np()).to(dev)
+    tab = {"nf4": WL.nf4_code_np, "fp4": WL.fp4_code_np, "int8": WL.int8_code_np,
+           "fp8_e4m3": WL.fp8_e4m3_code_np}[args.code]()
+    bits = 8 if args.code in ("int8", "fp8_e4m3") else 4
+    code = torch.from_numpy(tab).to(dev)
     ncode = torch.from_numpy(WL.nested_code_np()).to(dev)
     off = None
     if family == "olmoe":
@@ -660,7 +746,7 @@ def run_only(args):
         wts = []
         for l in range(L):
             w = WL.gpu_weight_f32(E * N, K, seed=70_000 + 16 * l + j, device=dev)
-            wts.append(api.nf4_quantize(w, code, ncode).per_expert(E))
+            wts.append(api.nf4_quantize(w, code, ncode, bits=bits).per_expert(E))
             del w
     else:
         projs = WL.LLAMA_8B if family == "llama" else WL.QWEN_32B
@@ -673,11 +759,11 @@ def run_only(args):
         wts = []
         for l in range(L):
             w = WL.gpu_weight_f32(N, K, seed=WL.stack_weight_seed(seed0, l, i), device=dev)
-            wts.append(api.nf4_quantize(w, code, ncode))
+            wts.append(api.nf4_quantize(w, code, ncode, bits=bits))
             del w
     ins = [WL.gpu_normal_bf16(M, K if d == "fwd" else N, seed=30_000 + l, device=dev) for l in range(L)]
     out = torch.empty((M, N if d == "fwd" else K), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(16, api.nf4_workspace_bytes(1, M, N, K), api.nf4_workspace_bytes(2, M, N, K)),
+    ws = torch.empty(max(16, *(api.nf4_workspace_bytes(op, M, N, K) for op in (1, 2, 5, 6))),
                      dtype=torch.uint8, device=dev)
 
     def one():
@@ -700,7 +786,7 @@ def run_only(args):
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-    print(json.dumps({"shape": f"{family}:{shape}", "M": M, "N": N, "K": K,
+    print(json.dumps({"shape": f"{family}:{shape}", "code": args.code, "M": M, "N": N, "K": K,
                       "experts": WL.OLMOE_E if off is not None else None,
                       "ops": L * (args.steps + args.warmup), "avg_us": round(ms * 1e3, 2),
                       "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
