@@ -1609,7 +1609,7 @@ struct GT {
   static constexpr int kA = BM * kPitch;                       // elements per buffer
   static constexpr int kAVec = BM * BK / 8 / kThreads;         // activation vectors per thread
   static constexpr int kDepth = 4;                             // steps held in registers
-  static constexpr bool kTrRead(bool trans) { return BITS == 4 && trans; }
+  static constexpr bool kTrRead(bool trans) { return trans; }
   // Eight waves: the transposed tile has unpadded rows whose 16-byte units
   // are XOR-swizzled by the row (256 columns: as in the ping-pong kernel; 128
   // columns: unit ^ 5 (row & 3)), so that the expansion's 16-byte writes (16
@@ -1777,12 +1777,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
       const uint32_t o0 = pack_bf16x2(__fmul_rn(scode[wd & 0xFFu], a), __fmul_rn(scode[(wd >> 8) & 0xFFu], a));
       const uint32_t o1 = pack_bf16x2(__fmul_rn(scode[(wd >> 16) & 0xFFu], a), __fmul_rn(scode[wd >> 24], a));
       if constexpr (TRANS) {
-        // element 4 d + e of the piece is W_hat[row wl, column 32 wq + 4 d + e]
-        const int c = 32 * wq + 4 * d;
-        bb[(c + 0) * P + wl] = static_cast<uint16_t>(o0);
-        bb[(c + 1) * P + wl] = static_cast<uint16_t>(o0 >> 16);
-        bb[(c + 2) * P + wl] = static_cast<uint16_t>(o1);
-        bb[(c + 3) * P + wl] = static_cast<uint16_t>(o1 >> 16);
+        // element 4 d + e of the piece is W_hat[row wl, column PW wq + 4 d + e]:
+        // four consecutive columns of contraction row wl of the [k][n] tile,
+        // which the transposed fragment reads take apart (as for NF4)
+        static_assert(TR && !SWZ, "8-bit input gradient: padded [k][n] tile");
+        *reinterpret_cast<u32x2_t*>(bb + wl * PT + G::PW * wq + 4 * d) = u32x2_t{o0, o1};
       } else {
         *reinterpret_cast<u32x2_t*>(bb + wl * P + 32 * wq + 4 * d) = u32x2_t{o0, o1};
       }
@@ -1954,7 +1953,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
     for (int j = 0; j < G::NI; ++j) {
       int64_t col = col0 + wn * G::WN + 32 * j + r32;
       // NF4 input gradient: tile column c holds output column 8 (c / 8) + pi(c % 8)
-      if constexpr (TR) col = (col & ~int64_t{7}) | (((col & 3) << 1) | ((col >> 2) & 1));
+      // (the 8-bit expansion keeps the column order)
+      if constexpr (TR && BITS == 4) col = (col & ~int64_t{7}) | (((col & 3) << 1) | ((col >> 2) & 1));
       if (col >= Nc) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
