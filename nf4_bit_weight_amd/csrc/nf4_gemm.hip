@@ -1907,17 +1907,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
   // register set and the buffer of every step are compile-time.
   constexpr int D = G::kDepth;
   static_assert(D == 2 || D == 4, "ring of 2 or 4 register sets, unrolled by 4");
+  // Every load is issued, also for steps past the last one, with the step
+  // index clamped to the last step (registers no step reads; load() clamps
+  // its addresses into the tensors anyway): with the loads under a branch
+  // the compiler could not count the loads issued after the ones a step
+  // needs and waited for all of them (vmcnt(0)) once every four steps,
+  // including the loads just issued for three steps ahead.
+  const int last = n > 0 ? n - 1 : 0;
   auto run = [&](auto act_c) __attribute__((always_inline)) {
     Regs R[D];
 #pragma unroll
-    for (int j = 0; j < D; ++j)
-      if (j < n) load(j, R[j]);
+    for (int j = 0; j < D; ++j) load(j < last ? j : last, R[j]);
     store(0, R[0]);
     __syncthreads();
     // step i = i0 + U of the unrolled body (i0 % 4 == 0)
     auto body = [&](auto u_c, int i) __attribute__((always_inline)) {
       constexpr int U = decltype(u_c)::value;
-      if (i + D < n) load(i + D, R[U % D]);
+      load(i + D < last ? i + D : last, R[U % D]);
       step(act_c, std::true_type{}, U & 1, R[(U + 1) % D]);
       __syncthreads();
     };
