@@ -1766,7 +1766,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemmt(GemmParams p) {
   };
   auto wscale = [&](const Regs& r) __attribute__((always_inline)) {
     float a;
-    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[r.sc & 0xFF], __uint_as_float(r.s2)), off);
+    // r.sc is a zero-extended byte here (loaded as uint8_t above)
+    if constexpr (NESTED) a = __fadd_rn(__fmul_rn(sncode[r.sc], __uint_as_float(r.s2)), off);
     else a = __uint_as_float(r.sc);
     return r.ok ? a : 0.f;
   };

@@ -129,10 +129,11 @@ def test_llama_decode_shapes(M, idx):
 def test_small_m_slices_and_chunks(M, rw, mp32, kw, z):
     """Every (row-group size, row groups, contraction slices, chunks) instance
     of the streaming kernels through the documented overrides: slices past a
-    short contraction hold no steps, and with four row groups the last
+    short contraction hold no steps, and with two row groups the last
     workgroup holds a row group past N.  (N and K are whole 16-row groups and
     256-column steps, the shapes the 16-row kernel takes; chunks of the
-    32-row kernel end inside its steps.)"""
+    32-row kernel end inside its steps.)  Four row groups are used only where
+    N is a multiple of 64 (here N = 304: the planner takes two instead)."""
     N, K = 304, 1536
     nested = (kw + z) % 2 == 0
     wq, wb, x = _setup(M, N, K, nested, 7 * kw + z + M)
@@ -163,6 +164,34 @@ def test_small_m_slices_and_chunks(M, rw, mp32, kw, z):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not bitwise repeatable"
     assert_close(y, O.matmul_fwd(xb, wb), f"y M={M} rw={rw} mp32={mp32} kw={kw} z={z}",
                  O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
+
+
+@pytest.mark.parametrize("nested", [False, True])
+@pytest.mark.parametrize("z", [1, 3])
+@pytest.mark.parametrize("M", [5, 24])
+def test_small_m_four_row_groups(M, z, nested):
+    """Four row groups per workgroup (two slices), N a multiple of 64 so that
+    every workgroup's row groups are whole, with and without chunks: two
+    calls bitwise equal and matching the oracle."""
+    N, K = 320, 1536
+    wq, wb, x = _setup(M, N, K, nested, 11 * M + z)
+    keys = ("NF4_GEMV_KW", "NF4_GEMV_Z", "NF4_GEMV_RW", "NF4_GEMV_MP32")
+    old = {k: os.environ.get(k) for k in keys}
+    os.environ.update({"NF4_GEMV_KW": "2", "NF4_GEMV_Z": str(z), "NF4_GEMV_RW": "4", "NF4_GEMV_MP32": "0"})
+    try:
+        xd = x.to(DEV)
+        y = api.nf4_matmul_fwd(xd, wq)
+        y2 = api.nf4_matmul_fwd(xd, wq)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not bitwise repeatable"
+    xb = WL.bf16_bits(x)
+    assert_close(y, O.matmul_fwd(xb, wb), f"y M={M} z={z}", O.matmul_fwd(abs_bits(xb), abs_bits(wb)), K)
 
 
 @pytest.mark.parametrize("kw", ["2", "4"])
