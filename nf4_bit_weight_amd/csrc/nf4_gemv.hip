@@ -847,16 +847,7 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
     // workgroups, takes 23.0 against 16.3)
     const int64_t wgs4 = (rg16 + 3) / 4 * z;
     if (M > 1 && (4 * wgs4 >= 3 * static_cast<int64_t>(cus) || (M > 8 && 2 * wgs4 >= cus))) rw = 4;
-    // Four row groups only where every workgroup's four are whole (N a
-    // multiple of 64, as in every Llama, Qwen and OLMoE projection): with a
-    // row group past N in the last workgroup that form came out not bitwise
-    // repeatable in some full test-suite runs (N = 304 and N = 300; never
-    // when run alone, cause not found), so two row groups (four slices)
-    // serve there.
-    if (rw == 4 && rg16 % 4 != 0) {
-      rw = 2;
-      kw = 4;
-    } else if (rw == 4) {
+    if (rw == 4) {
       kw = 2;
     } else {
       const int64_t wgs = rg16 * z;
@@ -865,7 +856,7 @@ void plan_small_m(GemmPlan& pl, int64_t M, int64_t N, int64_t K, int cus) {
   }
   // tuning override (documented): NF4_GEMV_RW (row groups per workgroup: 1 / 2 / 4 at M <= 16)
   const char* orw = getenv("NF4_GEMV_RW");
-  if (orw && pl.bm == 16 && (atoi(orw) == 1 || atoi(orw) == 2 || (atoi(orw) == 4 && rg16 % 4 == 0))) rw = atoi(orw);
+  if (orw && pl.bm == 16 && (atoi(orw) == 1 || atoi(orw) == 2 || atoi(orw) == 4)) rw = atoi(orw);
   pl.bn = rw;
   // the line-staged kernel holds two staging slots per wave: at most
   // kLnMaxWaves waves per workgroup; 32-row groups: 16
