@@ -404,7 +404,7 @@ __global__ __launch_bounds__(64 * (4 + 4 * C), 1) void k_gemm(GemmParams p) {
                "ds_read_b32 %2, %5 offset:" #OFF "\n\t"                                    \
                "ds_read_b32 %3, %5 offset:" #OFF "+1024\n\t"                               \
                "s_waitcnt lgkmcnt(0)"                                                      \
-               : "=v"(r.pk0), "=v"(r.pk1), "=v"(r.sc), "=v"(r.s2)                          \
+               : "=&v"(r.pk0), "=&v"(r.pk1), "=&v"(r.sc), "=&v"(r.s2)                      \
                : "v"(st_unit), "v"(st_scale)                                               \
                : "memory")
     auto read_unit = [&](int slot) {
@@ -854,7 +854,7 @@ __global__ __launch_bounds__(512, 1) void k_pp(GemmParams p) {
                "ds_read_b32 %1, %4 offset:" #OFF "\n\t"                                    \
                "ds_read_b32 %2, %4 offset:" #OFF "+1024\n\t"                               \
                "s_waitcnt lgkmcnt(0)"                                                      \
-               : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)                                        \
+               : "=&v"(r.pk), "=&v"(r.sc), "=&v"(r.s2)                                     \
                : "v"(st_pk), "v"(st_sc)                                                    \
                : "memory")
   auto read_unit = [&](int slot) __attribute__((always_inline)) {
@@ -1300,7 +1300,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void k_rb(GemmParams p) {
                  "ds_read_b32 %1, %4 offset:%5\n\t"
                  "ds_read_b32 %2, %4 offset:%6\n\t"
                  "s_waitcnt lgkmcnt(0)"
-                 : "=v"(r.pk), "=v"(r.sc), "=v"(r.s2)
+                 : "=&v"(r.pk), "=&v"(r.sc), "=&v"(r.s2)
                  : "v"(st_pk), "v"(st_sc), "i"(off), "i"(off + 256)
                  : "memory");
     if constexpr (!NESTED) r.s2 = 0;

@@ -587,7 +587,7 @@ __global__ __launch_bounds__(64 * RW * KW) void k_gemv_ln(GemvParams p) {
                "ds_read_b128 %1, %4 offset:" #OFF "\n\t"                                   \
                "ds_read_b32 %2, %5 offset:" #OFF "\n\t"                                    \
                "s_waitcnt lgkmcnt(0)"                                                      \
-               : "=v"(u.lo), "=v"(u.hi), "=v"(u.sc)                                        \
+               : "=&v"(u.lo), "=&v"(u.hi), "=&v"(u.sc)                                     \
                : "v"(a_lo), "v"(a_hi), "v"(a_sc)                                           \
                : "memory")
   auto read_slot = [&](auto slot_c) {

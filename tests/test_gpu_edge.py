@@ -120,7 +120,9 @@ def test_autograd_keeps_caller_dtype(dtype):
     y.float().sum().backward()
     assert x.grad.dtype == dtype
     ref = nf4_linear(x.detach().to(torch.bfloat16), wq)
-    assert torch.equal(y.to(torch.bfloat16).view(torch.int16), ref.view(torch.int16))
+    # the wrapper's output is the bf16 result cast to the caller's dtype: compare
+    # after the same cast (bf16 -> fp16 -> bf16 is not exact below 2^-17)
+    assert torch.equal(y, ref.to(dtype))
     E = 2
     wg, _ = _weight(E * N, K, True, 12)
     off = torch.tensor([0, 5, M], dtype=torch.int32, device=DEV)
