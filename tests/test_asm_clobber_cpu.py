@@ -73,6 +73,21 @@ def test_multi_load_asm_outputs_are_early_clobber():
     assert checked >= 4, "the slot and unit reads of the kernels were not found"
 
 
+def test_asm_loads_wait_in_their_own_block():
+    """An asm load whose result lands in a register must be waited for inside
+    the same block: the compiler takes the output as written when the block
+    ends, and could otherwise reuse or read that register while the load is
+    still in flight."""
+    checked = 0
+    for name, text in _sources():
+        for template, outputs in _asm_blocks(text):
+            if outputs and any(op in template for op in LOADS):
+                checked += 1
+                last_load = max(template.rfind(op) for op in LOADS)
+                assert "s_waitcnt" in template[last_load:], f"{name}: {template[:60]!r} returns before its loads land"
+    assert checked >= 5
+
+
 def test_checker_flags_a_plain_output():
     text = 'asm volatile("ds_read_b128 %0, %2\\n\\tds_read_b32 %1, %3" : "=v"(a), "=&v"(b) : "v"(p), "v"(q));'
     (template, outputs), = _asm_blocks(text)
